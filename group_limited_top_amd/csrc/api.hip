@@ -1,0 +1,338 @@
+// api.hip -- the C ABI of libmoe (include/moe.h): validation, workspace
+// layout and launch sequencing.  Everything here runs on the host; nothing
+// touches device memory before validation has passed.
+#include "moe.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace regions (byte offsets from ws).  One layout serves every entry
+// point; regions an entry point does not use are simply left alone.
+struct Layout {
+  size_t status;       // uint32 status word (first 256 bytes)
+  size_t split;        // bf16 [3][E][H] router weight parts (bf16 path)
+  size_t logits;       // fp32 [T][E]
+  size_t idx;          // int32 [T][K]
+  size_t w;            // fp32 [T][K]
+  size_t counts;       // int32 [E]
+  size_t offsets;      // int32 [E+1]
+  size_t sorted_pair;  // int32 [P]
+  size_t pair_slot;    // int32 [P]
+  size_t chunk_hist;   // int32 [nchunks][E]
+  size_t tile_off;     // int32 [E+2]
+  size_t h_routed;     // dtype [P][I]
+  size_t h_shared;     // dtype [T][Is]
+  size_t o_routed;     // dtype [P][H]
+  size_t o_shared;     // dtype [T][H]
+  size_t total;
+};
+
+Layout make_layout(const moe_desc_t& d) {
+  const size_t T = (size_t)d.T, H = (size_t)d.H, E = (size_t)d.E, K = (size_t)d.top_k;
+  const size_t P = T * K;
+  const size_t elt = d.dtype == MOE_BF16 ? 2 : 4;
+  const size_t nchunks = (P + moe::kPermuteChunk - 1) / moe::kPermuteChunk;
+  const size_t Is = (size_t)d.I_shared;
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.status = take(kAlign);
+  L.split = take(d.dtype == MOE_BF16 ? 3 * E * H * 2 : 0);
+  L.logits = take(T * E * 4);
+  L.idx = take(P * 4);
+  L.w = take(P * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted_pair = take(P * 4);
+  L.pair_slot = take(P * 4);
+  L.chunk_hist = take(nchunks * E * 4);
+  L.tile_off = take((E + 2) * 4);
+  L.h_routed = take(P * (size_t)d.I * elt);
+  L.h_shared = take(T * Is * elt);
+  L.o_routed = take(P * H * elt);
+  L.o_shared = take(Is > 0 ? T * H * elt : 0);
+  L.total = o;
+  return L;
+}
+
+int validate(const moe_desc_t* d) {
+  if (!d) return MOE_ERR_INVALID;
+  if (d->T < 0 || d->H <= 0 || d->E <= 0 || d->n_group <= 0 || d->topk_group <= 0 ||
+      d->top_k <= 0 || d->I <= 0 || d->I_shared < 0)
+    return MOE_ERR_INVALID;
+  if (d->E % d->n_group != 0) return MOE_ERR_INVALID;
+  const int gsize = d->E / d->n_group;
+  if (gsize < 2) return MOE_ERR_INVALID;
+  if (d->topk_group > d->n_group) return MOE_ERR_INVALID;
+  if ((int64_t)d->top_k > (int64_t)d->topk_group * gsize) return MOE_ERR_INVALID;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (!isfinite(d->routed_scaling_factor)) return MOE_ERR_INVALID;
+  if (d->flags & ~(MOE_F_WRITE_LOGITS | MOE_F_CHECK_FINITE)) return MOE_ERR_INVALID;
+  // kernel envelope
+  if (d->E > 512 || d->n_group > 64 || d->top_k > 16) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_BF16 && d->H % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_F32 && (d->H % 64 != 0 || d->H > 16384)) return MOE_ERR_UNSUPPORTED;
+  if (d->I % 64 != 0 || d->I > 1024) return MOE_ERR_UNSUPPORTED;
+  if (d->I_shared % 64 != 0 || d->I_shared > 1024) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d->T * d->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u) != 0; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+int check_ws(const moe_desc_t& d, void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < make_layout(d).total) return MOE_ERR_WORKSPACE;
+  if (misaligned(ws)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// route into (idx, w) with logits in `logits` (never NULL here)
+int run_route(const moe_desc_t& d, const void* x, const float* w_router, const float* bias,
+              float* logits, int32_t* idx, float* w, void* ws, hipStream_t s,
+              const moe::StageTimer* tm = nullptr) {
+  const Layout L = make_layout(d);
+  hipError_t e;
+  if (d.dtype == MOE_BF16) {
+    uint16_t* split = at<uint16_t>(ws, L.split);
+    e = moe::launch_split_router(w_router, split, d.E, d.H, s, tm);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_logits_bf16(reinterpret_cast<const uint16_t*>(x), split, logits, d.T, d.H, d.E,
+                                s, tm);
+  } else {
+    e = moe::launch_logits_f32(reinterpret_cast<const float*>(x), w_router, logits, d.T, d.H, d.E,
+                               s, tm);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_select(logits, bias, idx, w, at<uint32_t>(ws, L.status), d.T, d.E, d.n_group,
+                         d.topk_group, d.top_k, d.routed_scaling_factor,
+                         (d.flags & MOE_F_CHECK_FINITE) != 0, s, tm);
+  return hip_rc(e);
+}
+
+int run_permute(const moe_desc_t& d, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking, void* ws,
+                hipStream_t s, const moe::StageTimer* tm = nullptr) {
+  const Layout L = make_layout(d);
+  return hip_rc(moe::launch_permute(idx, (int64_t)d.T * d.top_k, d.E, at<int32_t>(ws, L.chunk_hist),
+                                    counts, offsets, sorted_pair, pair_slot, tracking,
+                                    at<uint32_t>(ws, L.status), s, tm));
+}
+
+int run_experts(const moe_desc_t& d, const void* x, const float* topk_w, const int32_t* offsets,
+                const int32_t* sorted_pair, const int32_t* pair_slot, const moe_weights_t& W,
+                void* y, void* ws, hipStream_t s, const moe::StageTimer* tm = nullptr) {
+  const Layout L = make_layout(d);
+  moe::ExpertArgs a;
+  a.T = d.T;
+  a.H = d.H;
+  a.E = d.E;
+  a.K = d.top_k;
+  a.I = d.I;
+  a.Is = d.I_shared;
+  a.x = x;
+  a.topk_w = topk_w;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.pair_slot = pair_slot;
+  a.w_gate = W.w_gate;
+  a.w_up = W.w_up;
+  a.w_down = W.w_down;
+  a.ws_gate = W.ws_gate;
+  a.ws_up = W.ws_up;
+  a.ws_down = W.ws_down;
+  a.y = y;
+  a.tile_off = at<int32_t>(ws, L.tile_off);
+  a.h_routed = at<void>(ws, L.h_routed);
+  a.h_shared = at<void>(ws, L.h_shared);
+  a.o_routed = at<void>(ws, L.o_routed);
+  a.o_shared = at<void>(ws, L.o_shared);
+  return hip_rc(d.dtype == MOE_BF16 ? moe::launch_experts_bf16(a, s, tm)
+                                    : moe::launch_experts_f32(a, s, tm));
+}
+
+int check_weights(const moe_desc_t& d, const moe_weights_t* W, bool need_router) {
+  if (!W) return MOE_ERR_INVALID;
+  if (need_router && !W->w_router) return MOE_ERR_INVALID;
+  if (!W->w_gate || !W->w_up || !W->w_down) return MOE_ERR_INVALID;
+  const bool has_shared = W->ws_gate || W->ws_up || W->ws_down;
+  if (d.I_shared > 0 && (!W->ws_gate || !W->ws_up || !W->ws_down)) return MOE_ERR_INVALID;
+  if (d.I_shared == 0 && has_shared) return MOE_ERR_INVALID;
+  const void* ps[] = {W->w_router, W->expert_bias, W->w_gate, W->w_up,
+                      W->w_down,   W->ws_gate,     W->ws_up,  W->ws_down};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc_t* desc) {
+  if (validate(desc) != MOE_OK) return 0;
+  return make_layout(*desc).total;
+}
+
+int moe_route(const moe_desc_t* desc, const void* x, const float* w_router,
+              const float* expert_bias, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+              size_t ws_bytes, hipStream_t stream) {
+  int rc = validate(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID;
+  if ((rc = check_ws(*desc, ws, ws_bytes))) return rc;
+  const void* ps[] = {x, w_router, expert_bias, logits, topk_idx, topk_w};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  float* lg = logits ? logits : at<float>(ws, make_layout(*desc).logits);
+  return run_route(*desc, x, w_router, expert_bias, lg, topk_idx, topk_w, ws, stream);
+}
+
+int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = validate(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!topk_idx || !counts || !offsets || !sorted_pair || !pair_slot) return MOE_ERR_INVALID;
+  if ((rc = check_ws(*desc, ws, ws_bytes))) return rc;
+  const void* ps[] = {topk_idx, counts, offsets, sorted_pair, pair_slot, tracking};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  return run_permute(*desc, topk_idx, counts, offsets, sorted_pair, pair_slot, tracking, ws,
+                     stream);
+}
+
+int moe_experts(const moe_desc_t* desc, const void* x, const float* topk_w,
+                const int32_t* offsets, const int32_t* sorted_pair, const int32_t* pair_slot,
+                const moe_weights_t* weights, void* y, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  int rc = validate(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x || !topk_w || !offsets || !sorted_pair || !pair_slot || !y) return MOE_ERR_INVALID;
+  if (x == y) return MOE_ERR_INVALID;
+  if ((rc = check_weights(*desc, weights, false))) return rc;
+  if ((rc = check_ws(*desc, ws, ws_bytes))) return rc;
+  const void* ps[] = {x, topk_w, offsets, sorted_pair, pair_slot, y};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  return run_experts(*desc, x, topk_w, offsets, sorted_pair, pair_slot, *weights, y, ws, stream);
+}
+
+}  // extern "C"
+
+static int layer_forward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                         void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                         int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
+                         hipStream_t stream, const moe::StageTimer* tm) {
+  int rc = validate(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x || !y || x == y) return MOE_ERR_INVALID;
+  if ((rc = check_weights(*desc, weights, true))) return rc;
+  if ((rc = check_ws(*desc, ws, ws_bytes))) return rc;
+  const void* ps[] = {x, y, topk_idx_out, topk_w_out, logits_out, counts_out, tracking};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  const moe_desc_t& d = *desc;
+  const Layout L = make_layout(d);
+  float* lg = (logits_out && (d.flags & MOE_F_WRITE_LOGITS)) ? logits_out : at<float>(ws, L.logits);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sp = at<int32_t>(ws, L.sorted_pair);
+  int32_t* ps_ = at<int32_t>(ws, L.pair_slot);
+  if ((rc = run_route(d, x, weights->w_router, weights->expert_bias, lg, idx, w, ws, stream, tm)))
+    return rc;
+  if ((rc = run_permute(d, idx, counts, offsets, sp, ps_, tracking, ws, stream, tm))) return rc;
+  return run_experts(d, x, w, offsets, sp, ps_, *weights, y, ws, stream, tm);
+}
+
+extern "C" {
+
+int moe_layer_forward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                      void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                      int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  return layer_forward(desc, x, weights, y, topk_idx_out, topk_w_out, logits_out, counts_out,
+                       tracking, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_forward_timed(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                            void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                            int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
+                            hipStream_t stream, int stage, hipEvent_t start, hipEvent_t stop) {
+  if (stage < 0 || stage >= MOE_NUM_STAGES || !start || !stop) return MOE_ERR_INVALID;
+  moe::StageTimer tm;
+  tm.stage = stage;
+  tm.start = start;
+  tm.stop = stop;
+  return layer_forward(desc, x, weights, y, topk_idx_out, topk_w_out, logits_out, counts_out,
+                       tracking, ws, ws_bytes, stream, &tm);
+}
+
+int moe_residual_rmsnorm(const moe_desc_t* desc, const void* x_in, const void* y, void* x_out,
+                         void* r_out, float eps, hipStream_t stream) {
+  int rc = validate(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x_in || !x_out || !r_out || !(eps >= 0.0f)) return MOE_ERR_INVALID;
+  const void* ps[] = {x_in, y, x_out, r_out};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  return hip_rc(moe::launch_residual_rmsnorm(desc->dtype == MOE_BF16, x_in, y, x_out, r_out, desc->T,
+                                             desc->H, eps, stream));
+}
+
+int moe_status(void* ws, size_t ws_bytes, hipStream_t stream, uint32_t* status) {
+  if (!ws || !status || ws_bytes < kAlign) return MOE_ERR_INVALID;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(ws, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return MOE_ERR_HIP;
+  *status = v;
+  return MOE_OK;
+}
+
+int moe_sigmoid32(const float* z, float* s, int64_t n, hipStream_t stream) {
+  if (n < 0) return MOE_ERR_INVALID;
+  if (n == 0) return MOE_OK;
+  if (!z || !s) return MOE_ERR_INVALID;
+  if (misaligned(z) || misaligned(s)) return MOE_ERR_ALIGN;
+  return hip_rc(moe::launch_sigmoid32(z, s, n, stream));
+}
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "success";
+    case MOE_ERR_INVALID: return "invalid argument (null pointer, negative size or inconsistent shape)";
+    case MOE_ERR_UNSUPPORTED: return "shape outside the kernels' supported envelope";
+    case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_size()";
+    case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MOE_ERR_HIP: return "a HIP launch or runtime call failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

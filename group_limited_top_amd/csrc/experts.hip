@@ -1,0 +1,554 @@
+// experts.hip -- grouped SwiGLU experts, shared expert and weighted combine.
+//
+// [Routing §四]: gate_proj, up_proj and down_proj are each one stacked
+// [E][I][H] tensor; every expert is down(silu(gate x) * up x).  [Routing §五]:
+// the shared expert has the same form, runs on every token and is added to the
+// weighted routed sum with no weight.
+//
+// Row space.  The T*K pairs are processed in expert-sorted order (row q of
+// expert e is pair sorted_pair[q], q in [offsets[e], offsets[e+1])); the shared
+// expert is handled as one more "expert" E whose rows are the T tokens.  Work
+// is cut into tiles of kTileRows rows of one expert; the tile list is built on
+// the device from offsets (no host synchronisation), and the launch grid is
+// sized for the worst case (blocks past the last tile exit at once).
+//
+// Weight-streaming kernels (bf16).  With few rows per expert the projections
+// are bound by reading the 1.5 GB of stacked weights once.  Each block owns a
+// slice of one expert's weights and streams it straight from HBM into
+// registers in MFMA operand layout, while the (few) token rows sit in LDS:
+//   gate/up: A = weight rows (I index) with K = H contiguous, B = token rows;
+//   down:    A = W_down^T; W_down[e] is [I][H] (H contiguous), so each lane
+//            loads 8 consecutive h of 8 consecutive i and transposes the 8x8
+//            bf16 block in registers, giving 8 MFMA tiles whose row m maps to
+//            h = h0 + 8m + j.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is) {
+  const int64_t P = T * K;
+  int64_t n = (P + kTileRows - 1) / kTileRows + E;
+  if (Is > 0) n += (T + kTileRows - 1) / kTileRows;
+  return n;
+}
+
+// tile_off[g] = number of tiles of "experts" 0..g-1 (E + 1 of them, the last
+// is the shared expert with T rows when Is > 0); tile_off[E + 1] = total.
+__global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offsets, int E, int T,
+                                                 int Is, int32_t* __restrict__ tile_off) {
+  __shared__ int32_t sc[1024];
+  const int g = threadIdx.x;
+  int32_t n = 0;
+  if (g < E) n = (offsets[g + 1] - offsets[g] + kTileRows - 1) / kTileRows;
+  else if (g == E && Is > 0) n = (T + kTileRows - 1) / kTileRows;
+  sc[g] = n;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int32_t add = (g >= d) ? sc[g - d] : 0;
+    __syncthreads();
+    sc[g] += add;
+    __syncthreads();
+  }
+  if (g <= E) tile_off[g] = sc[g] - n;
+  if (g == E) tile_off[E + 1] = sc[g];
+}
+
+struct TileInfo {
+  int e;       // expert, E = shared
+  bool shared;
+  int row0;    // first row (sorted pair row, or token for the shared expert)
+  int nrows;   // rows in this tile, 1..kTileRows
+};
+
+// Returns false when `tile` is past the last tile.
+__device__ __forceinline__ bool decode_tile(const ExpertArgs& a, int tile, TileInfo& ti) {
+  if (tile >= a.tile_off[a.E + 1]) return false;
+  const int e = upper_bound_i32(a.tile_off, a.E + 2, tile) - 1;
+  const int m = tile - a.tile_off[e];
+  ti.e = e;
+  ti.shared = (e == a.E);
+  if (ti.shared) {
+    ti.row0 = m * kTileRows;
+    ti.nrows = min(kTileRows, a.T - ti.row0);
+  } else {
+    ti.row0 = a.offsets[e] + m * kTileRows;
+    ti.nrows = min(kTileRows, a.offsets[e + 1] - ti.row0);
+  }
+  return true;
+}
+
+// ----------------------------------------------------------------------------
+// gate/up + SwiGLU, bf16.  Block: 4 waves, one tile of rows, 64 consecutive
+// intermediate rows i (16 per wave) of both gate and up.  K = H is streamed in
+// chunks of 256: weights go global -> registers (double-buffered), token rows
+// global -> LDS (double-buffered).
+// ----------------------------------------------------------------------------
+constexpr int kGuChunk = 256;
+constexpr int kGuRowU4 = kGuChunk / 8 + 1;  // 16-byte units per LDS row (+1: bank spread)
+constexpr int kSub = kTileRows / 16;       // 16-row MFMA sub-tiles per tile
+
+__global__ __launch_bounds__(256, 2) void k_gateup_bf16(const ExpertArgs a, int slices) {
+  __shared__ u32x4 xs[2][kTileRows][kGuRowU4];
+  const int slice = blockIdx.x % slices;
+  TileInfo ti;
+  if (!decode_tile(a, blockIdx.x / slices, ti)) return;
+  const int I = ti.shared ? a.Is : a.I;
+  const int i0 = slice * 64;
+  if (i0 >= I) return;
+  const int H = a.H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  // token-row staging: thread -> (row, 4 x 16 B of the chunk)
+  const int sr = threadIdx.x >> 3, sc = (threadIdx.x & 7) * 4;
+  const uint16_t* xrow = nullptr;
+  if (sr < ti.nrows) {
+    const int tok = ti.shared ? ti.row0 + sr : a.sorted_pair[ti.row0 + sr] / a.K;
+    xrow = reinterpret_cast<const uint16_t*>(a.x) + (size_t)tok * H;
+  }
+  // weight rows of this lane
+  const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
+  const int wrow = i0 + wave * 16 + r16;
+  const uint16_t* wg = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_gate : a.w_gate) + ebase +
+                       (size_t)wrow * H + q * 8;
+  const uint16_t* wu = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_up : a.w_up) + ebase +
+                       (size_t)wrow * H + q * 8;
+
+  const int nchunks = H / kGuChunk;
+  const int nsub = (ti.nrows + 15) >> 4;
+  u32x4 ga[8], ua[8], gb[8], ub[8], xst[4];
+  f32x4 accg[kSub], accu[kSub];
+#pragma unroll
+  for (int n = 0; n < kSub; ++n) {
+    accg[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  auto load_w = [&](u32x4* g, u32x4* u, int c) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      g[s] = ld16_stream(wg + c * kGuChunk + s * 32);
+      u[s] = ld16_stream(wu + c * kGuChunk + s * 32);
+    }
+  };
+  auto load_x = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xst[i] = xrow ? ld16(xrow + c * kGuChunk + (sc + i) * 8) : zero4;
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs[buf][sr][sc + i] = xst[i];
+  };
+  auto compute = [&](const u32x4* g, const u32x4* u, int buf) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int n = 0; n < kSub; ++n) {
+        if (n < nsub) {
+          const u32x4 b = xs[buf][n * 16 + r16][s * 4 + q];
+          accg[n] = mfma16x16x32(g[s], b, accg[n]);
+          accu[n] = mfma16x16x32(u[s], b, accu[n]);
+        }
+      }
+    }
+  };
+
+  load_w(ga, ua, 0);
+  load_x(0);
+  store_x(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    if (c + 1 < nchunks) {
+      load_w(gb, ub, c + 1);
+      load_x(c + 1);
+    }
+    compute(ga, ua, 0);
+    if (c + 1 < nchunks) store_x(1);
+    __syncthreads();
+    if (c + 1 >= nchunks) break;
+    if (c + 2 < nchunks) {
+      load_w(ga, ua, c + 2);
+      load_x(c + 2);
+    }
+    compute(gb, ub, 1);
+    if (c + 2 < nchunks) store_x(0);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows i = i0 + 16*wave + 4q + 0..3 of token row n*16 + r16
+  uint16_t* hbase = reinterpret_cast<uint16_t*>(ti.shared ? a.h_shared : a.h_routed);
+  const int ib = i0 + wave * 16 + 4 * q;
+#pragma unroll
+  for (int n = 0; n < kSub; ++n) {
+    const int row = n * 16 + r16;
+    if (n < nsub && row < ti.nrows) {
+      float hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = silu_f32(accg[n][i]) * accu[n][i];
+      u32x2 pk;
+      pk.x = pack_bf16x2(hv[0], hv[1]);
+      pk.y = pack_bf16x2(hv[2], hv[3]);
+      *reinterpret_cast<u32x2*>(hbase + (size_t)(ti.row0 + row) * I + ib) = pk;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// down, bf16.  Block: 4 waves, one tile of rows, 512 output columns (128 per
+// wave).  The tile's hidden rows h [rows][I] sit in LDS; W_down streams from
+// HBM 8 x 16 B per lane per 32-deep k step and is transposed in registers.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&v)[8], u32x4 (&a)[8]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t x0 = v[2 * c][jj], x1 = v[2 * c + 1][jj];
+      a[2 * jj][c] = (x0 & 0xffffu) | (x1 << 16);
+      a[2 * jj + 1][c] = (x0 >> 16) | (x1 & 0xffff0000u);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_down_bf16(const ExpertArgs a, int hslices) {
+  extern __shared__ u32x4 hs[];  // [kTileRows][I/8 + 1]
+  const int hslice = blockIdx.x % hslices;
+  TileInfo ti;
+  if (!decode_tile(a, blockIdx.x / hslices, ti)) return;
+  const int I = ti.shared ? a.Is : a.I;
+  const int H = a.H;
+  const int RS = I / 8 + 1;
+  const uint16_t* hsrc = reinterpret_cast<const uint16_t*>(ti.shared ? a.h_shared : a.h_routed);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int v = threadIdx.x; v < kTileRows * (I / 8); v += 256) {
+    const int r = v / (I / 8), c = v % (I / 8);
+    hs[r * RS + c] = (r < ti.nrows) ? ld16(hsrc + (size_t)(ti.row0 + r) * I + c * 8) : zero4;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int h0 = hslice * 512 + wave * 128;
+  if (h0 >= H) return;  // no barrier below
+  const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
+  const uint16_t* wd = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_down : a.w_down) + ebase +
+                       (size_t)(q * 8) * H + h0 + 8 * r16;
+  const int nsub = (ti.nrows + 15) >> 4;
+  f32x4 acc[8][kSub];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int n = 0; n < kSub; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 va[8], vb[8], am[8];
+  auto load = [&](u32x4 (&v)[8], int k0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = ld16_stream(wd + (size_t)(k0 + r) * H);
+  };
+  auto step = [&](const u32x4 (&v)[8], int k0) {
+    transpose8x8_bf16(v, am);
+#pragma unroll
+    for (int n = 0; n < kSub; ++n) {
+      if (n < nsub) {
+        const u32x4 b = hs[(n * 16 + r16) * RS + k0 / 8 + q];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j][n] = mfma16x16x32(am[j], b, acc[j][n]);
+      }
+    }
+  };
+  load(va, 0);
+  for (int k0 = 0; k0 < I; k0 += 64) {
+    if (k0 + 32 < I) load(vb, k0 + 32);
+    step(va, k0);
+    if (k0 + 32 >= I) break;
+    if (k0 + 64 < I) load(va, k0 + 64);
+    step(vb, k0 + 32);
+  }
+
+  // epilogue: tile j, C row 4q+i -> h = h0 + 8*(4q+i) + j; 8 consecutive h per (n, i)
+  uint16_t* obase = reinterpret_cast<uint16_t*>(ti.shared ? a.o_shared : a.o_routed);
+#pragma unroll
+  for (int n = 0; n < kSub; ++n) {
+    const int row = n * 16 + r16;
+    if (n < nsub && row < ti.nrows) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 pk;
+        pk.x = pack_bf16x2(acc[0][n][i], acc[1][n][i]);
+        pk.y = pack_bf16x2(acc[2][n][i], acc[3][n][i]);
+        pk.z = pack_bf16x2(acc[4][n][i], acc[5][n][i]);
+        pk.w = pack_bf16x2(acc[6][n][i], acc[7][n][i]);
+        st16(obase + (size_t)(ti.row0 + row) * H + h0 + 8 * (4 * q + i), pk);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// combine, bf16: y[t] = o_shared[t] + sum_j w[t][j] * o_routed[pair_slot[t*K+j]]
+// in j order, fp32, one rounding.  [Routing §四] (weighted sum), §五 (shared
+// output added as is).
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
+  const int t = blockIdx.x;
+  const int H = a.H, K = a.K;
+  const uint16_t* osh = reinterpret_cast<const uint16_t*>(a.o_shared);
+  const uint16_t* orr = reinterpret_cast<const uint16_t*>(a.o_routed);
+  uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
+  for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
+    float acc[8];
+    if (a.Is > 0) {
+      const u32x4 v = ld16(osh + (size_t)t * H + c * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = bf16_lo(v[i]);
+        acc[2 * i + 1] = bf16_hi(v[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    }
+    for (int j = 0; j < K; ++j) {
+      const int32_t slot = a.pair_slot[(size_t)t * K + j];
+      if (slot < 0) continue;
+      const float w = a.topk_w[(size_t)t * K + j];
+      const u32x4 v = ld16(orr + (size_t)slot * H + c * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = acc[2 * i] + w * bf16_lo(v[i]);
+        acc[2 * i + 1] = acc[2 * i + 1] + w * bf16_hi(v[i]);
+      }
+    }
+    u32x4 pk;
+    pk.x = pack_bf16x2(acc[0], acc[1]);
+    pk.y = pack_bf16x2(acc[2], acc[3]);
+    pk.z = pack_bf16x2(acc[4], acc[5]);
+    pk.w = pack_bf16x2(acc[6], acc[7]);
+    st16(y + (size_t)t * H + c * 8, pk);
+  }
+}
+
+hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
+  // the down kernel's LDS tile can exceed the 64 KiB default for I > 960
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_down_bf16), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kTileRows * (1024 / 8 + 1) * 16);
+  if (attr != hipSuccess) return attr;
+  stage_begin(tm, kTiles, s);
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
+  stage_end(tm, kTiles, s);
+  const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is);
+  const int imax = a.I > a.Is ? a.I : a.Is;
+  const int slices = imax / 64;
+  stage_begin(tm, kGateUp, s);
+  hipLaunchKernelGGL(k_gateup_bf16, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
+  stage_end(tm, kGateUp, s);
+  const int hslices = (a.H + 511) / 512;
+  const size_t lds = (size_t)kTileRows * (imax / 8 + 1) * 16;
+  stage_begin(tm, kDown, s);
+  hipLaunchKernelGGL(k_down_bf16, dim3((unsigned)(tiles * hslices)), dim3(256), lds, s, a, hslices);
+  stage_end(tm, kDown, s);
+  stage_begin(tm, kCombine, s);
+  hipLaunchKernelGGL(k_combine_bf16, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  stage_end(tm, kCombine, s);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// fp32 variants (small fp32 layers): LDS-tiled fp32 FMA.
+// ----------------------------------------------------------------------------
+// gate/up: block = tile rows (32) x 64 intermediate rows; thread = (row, 8 i).
+__global__ __launch_bounds__(256) void k_gateup_f32(const ExpertArgs a, int slices) {
+  __shared__ float xs[kTileRows][65];
+  __shared__ float gs[64][65];
+  __shared__ float us[64][65];
+  const int slice = blockIdx.x % slices;
+  TileInfo ti;
+  if (!decode_tile(a, blockIdx.x / slices, ti)) return;
+  const int I = ti.shared ? a.Is : a.I;
+  const int i0 = slice * 64;
+  if (i0 >= I) return;
+  const int H = a.H;
+  const float* x = reinterpret_cast<const float*>(a.x);
+  const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
+  const float* Wg = reinterpret_cast<const float*>(ti.shared ? a.ws_gate : a.w_gate) + ebase;
+  const float* Wu = reinterpret_cast<const float*>(ti.shared ? a.ws_up : a.w_up) + ebase;
+  const int row = threadIdx.x >> 3, cg = threadIdx.x & 7;
+  float accg[8], accu[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) accg[c] = accu[c] = 0.0f;
+  for (int k0 = 0; k0 < H; k0 += 64) {
+    for (int v = threadIdx.x; v < kTileRows * 64; v += 256) {
+      const int r = v >> 6, k = v & 63;
+      float val = 0.0f;
+      if (r < ti.nrows) {
+        const int tok = ti.shared ? ti.row0 + r : a.sorted_pair[ti.row0 + r] / a.K;
+        val = x[(size_t)tok * H + k0 + k];
+      }
+      xs[r][k] = val;
+    }
+    for (int v = threadIdx.x; v < 64 * 64; v += 256) {
+      const int i = v >> 6, k = v & 63;
+      gs[i][k] = Wg[(size_t)(i0 + i) * H + k0 + k];
+      us[i][k] = Wu[(size_t)(i0 + i) * H + k0 + k];
+    }
+    __syncthreads();
+    for (int k = 0; k < 64; ++k) {
+      const float xv = xs[row][k];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        accg[c] = __builtin_fmaf(xv, gs[cg * 8 + c][k], accg[c]);
+        accu[c] = __builtin_fmaf(xv, us[cg * 8 + c][k], accu[c]);
+      }
+    }
+    __syncthreads();
+  }
+  if (row < ti.nrows) {
+    float* h = reinterpret_cast<float*>(ti.shared ? a.h_shared : a.h_routed);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      h[(size_t)(ti.row0 + row) * I + i0 + cg * 8 + c] = silu_f32(accg[c]) * accu[c];
+  }
+}
+
+// down: block = tile rows (32) x 256 output columns; thread = (row, 32 columns
+// cg + 8c).
+__global__ __launch_bounds__(256) void k_down_f32(const ExpertArgs a, int hslices) {
+  __shared__ float hsm[kTileRows][33];
+  __shared__ float ws[32][256];
+  const int hslice = blockIdx.x % hslices;
+  TileInfo ti;
+  if (!decode_tile(a, blockIdx.x / hslices, ti)) return;
+  const int I = ti.shared ? a.Is : a.I;
+  const int H = a.H;
+  const int h0 = hslice * 256;
+  const float* hsrc = reinterpret_cast<const float*>(ti.shared ? a.h_shared : a.h_routed);
+  const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
+  const float* Wd = reinterpret_cast<const float*>(ti.shared ? a.ws_down : a.w_down) + ebase;
+  const int row = threadIdx.x >> 3, cg = threadIdx.x & 7;
+  float acc[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
+  for (int k0 = 0; k0 < I; k0 += 32) {
+    for (int v = threadIdx.x; v < kTileRows * 32; v += 256) {
+      const int r = v >> 5, k = v & 31;
+      hsm[r][k] = (r < ti.nrows) ? hsrc[(size_t)(ti.row0 + r) * I + k0 + k] : 0.0f;
+    }
+    for (int v = threadIdx.x; v < 32 * 256; v += 256) {
+      const int k = v >> 8, c = v & 255;
+      ws[k][c] = (h0 + c < H) ? Wd[(size_t)(k0 + k) * H + h0 + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int k = 0; k < 32; ++k) {
+      const float hv = hsm[row][k];
+#pragma unroll
+      for (int c = 0; c < 32; ++c) acc[c] = __builtin_fmaf(hv, ws[k][cg + 8 * c], acc[c]);
+    }
+    __syncthreads();
+  }
+  if (row < ti.nrows) {
+    float* o = reinterpret_cast<float*>(ti.shared ? a.o_shared : a.o_routed);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const int h = h0 + cg + 8 * c;
+      if (h < H) o[(size_t)(ti.row0 + row) * H + h] = acc[c];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_combine_f32(const ExpertArgs a) {
+  const int t = blockIdx.x;
+  const int H = a.H, K = a.K;
+  const float* osh = reinterpret_cast<const float*>(a.o_shared);
+  const float* orr = reinterpret_cast<const float*>(a.o_routed);
+  float* y = reinterpret_cast<float*>(a.y);
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float acc = (a.Is > 0) ? osh[(size_t)t * H + h] : 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const int32_t slot = a.pair_slot[(size_t)t * K + j];
+      if (slot < 0) continue;
+      acc = acc + a.topk_w[(size_t)t * K + j] * orr[(size_t)slot * H + h];
+    }
+    y[(size_t)t * H + h] = acc;
+  }
+}
+
+hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
+  stage_begin(tm, kTiles, s);
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
+  stage_end(tm, kTiles, s);
+  const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is);
+  const int imax = a.I > a.Is ? a.I : a.Is;
+  const int slices = imax / 64;
+  stage_begin(tm, kGateUp, s);
+  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
+  stage_end(tm, kGateUp, s);
+  const int hslices = (a.H + 255) / 256;
+  stage_begin(tm, kDown, s);
+  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(256), 0, s, a, hslices);
+  stage_end(tm, kDown, s);
+  stage_begin(tm, kCombine, s);
+  hipLaunchKernelGGL(k_combine_f32, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  stage_end(tm, kCombine, s);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// residual + RMSNorm (for stacking layers; gamma = 1), one block per row
+// ----------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_residual_rmsnorm(const void* x_in, const void* y,
+                                                           void* x_out, void* r_out, int H,
+                                                           float eps) {
+  __shared__ float red[256];
+  const int t = blockIdx.x;
+  float ss = 0.0f;
+  // pass 1: x_out = RN(x + y), sum of squares of the rounded values
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    const size_t i = (size_t)t * H + h;
+    float v;
+    if (BF16) {
+      v = bf16_to_f32(reinterpret_cast<const uint16_t*>(x_in)[i]);
+      if (y) v = v + bf16_to_f32(reinterpret_cast<const uint16_t*>(y)[i]);
+      const uint32_t b = f32_to_bf16_bits(v);
+      reinterpret_cast<uint16_t*>(x_out)[i] = (uint16_t)b;
+      v = bf16_to_f32((uint16_t)b);
+    } else {
+      v = reinterpret_cast<const float*>(x_in)[i];
+      if (y) v = v + reinterpret_cast<const float*>(y)[i];
+      reinterpret_cast<float*>(x_out)[i] = v;
+    }
+    ss = __builtin_fmaf(v, v, ss);
+  }
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int d = 128; d > 0; d >>= 1) {
+    if (threadIdx.x < d) red[threadIdx.x] += red[threadIdx.x + d];
+    __syncthreads();
+  }
+  const float inv = 1.0f / sqrtf(red[0] / (float)H + eps);
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    const size_t i = (size_t)t * H + h;
+    if (BF16) {
+      const float v = bf16_to_f32(reinterpret_cast<const uint16_t*>(x_out)[i]);
+      reinterpret_cast<uint16_t*>(r_out)[i] = (uint16_t)f32_to_bf16_bits(v * inv);
+    } else {
+      const float v = reinterpret_cast<const float*>(x_out)[i];
+      reinterpret_cast<float*>(r_out)[i] = v * inv;
+    }
+  }
+}
+
+hipError_t launch_residual_rmsnorm(bool bf16, const void* x_in, const void* y, void* x_out,
+                                   void* r_out, int T, int H, float eps, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(k_residual_rmsnorm<true>, dim3((unsigned)T), dim3(256), 0, s, x_in, y, x_out,
+                       r_out, H, eps);
+  else
+    hipLaunchKernelGGL(k_residual_rmsnorm<false>, dim3((unsigned)T), dim3(256), 0, s, x_in, y,
+                       x_out, r_out, H, eps);
+  return hipGetLastError();
+}
+
+}  // namespace moe

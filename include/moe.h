@@ -1,0 +1,211 @@
+/* moe.h -- C ABI of libmoe: the forward pass of a group-limited top-k
+ * sparse-MoE layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the page "InternLumina-U2中256个专家的路由
+ * 秘密：分组受限Top-K、Expert Bias与Fused MoE详解" (cited [Routing §n], n its
+ * numbered section):
+ *   [Routing §二 step 1]  per-expert sigmoid scores of fp32 router logits;
+ *   [Routing §二 step 2]  group-limited top-k: experts cut in index order into
+ *                         n_group groups, group score = sum of the group's two
+ *                         best scores, keep topk_group groups, top_k of those;
+ *   [Routing §三]         expert_bias added to the scores for selection only;
+ *   [Routing §二 step 3]  weights = unbiased scores / (their sum + 1e-20),
+ *                         times routed_scaling_factor;
+ *   [Routing §四]         stacked [E][I][H] SwiGLU experts;
+ *   [Routing §五]         one shared expert added with no weight;
+ *   [Routing §六]         per-expert hit counts (bincount of the choices).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) are device memory of the current HIP device;
+ *    (host) are host memory.  Arrays are row-major and contiguous; every
+ *    device pointer must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
+ *  - Calls are asynchronous on `stream` and never synchronise, except
+ *    moe_status.  The library keeps no pointer after a call returns and holds
+ *    no mutable global state; concurrent calls on different workspaces are
+ *    safe.  It allocates no memory: scratch space is the caller's workspace.
+ *  - Results are deterministic: identical inputs give bit-identical outputs
+ *    (no floating-point atomics anywhere).
+ *  - Every error is detected on the host before anything is enqueued; on an
+ *    error nothing is launched and no output is touched.  T = 0 is a no-op
+ *    success.  Inputs are never written.  Outputs are fully overwritten,
+ *    except `tracking`, which accumulates.
+ *  - A selection tie goes to the lower group index, then to the lower expert
+ *    index; the top_k chosen experts are returned in descending biased score.
+ *  - sigma32, the router sigmoid, is specified exactly: the fp32 rounding
+ *    (round to nearest even) of 1 / (1 + E(-z)) evaluated in IEEE fp64, where
+ *    E(t) = 2^n * P(r), n = rint(t * RN(log2 e)), r = fma(-n, L2, fma(-n, L1, t))
+ *    with L1 = RN(ln 2), L2 = RN(ln 2 - L1) (Cody & Waite reduction) and P the
+ *    degree-13 Taylor polynomial of exp with coefficients RN(1/i!) by Horner
+ *    fma; -z > 104 gives +0, -z < -40 gives 1, NaN gives NaN.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes -------------------------------------------------------- */
+#define MOE_OK 0
+#define MOE_ERR_INVALID (-1)     /* null required pointer, negative size, inconsistent shape */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid, but outside the kernels' envelope (see below) */
+#define MOE_ERR_WORKSPACE (-3)   /* ws is NULL or ws_bytes < moe_workspace_size(desc) */
+#define MOE_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
+#define MOE_ERR_HIP (-5)         /* a HIP call failed; moe_strerror gives no HIP code */
+
+/* ---- dtypes and flags ---------------------------------------------------- */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+#define MOE_F_WRITE_LOGITS 1u /* moe_layer_forward writes logits_out (otherwise ignored) */
+#define MOE_F_CHECK_FINITE 2u /* record non-finite router logits in the status word */
+
+/* Status word bits, read by moe_status.  The first 256 bytes of a workspace
+ * hold the status word: zero them before the workspace's first use. */
+#define MOE_STATUS_NONFINITE 1u /* some token had a NaN/Inf router logit */
+#define MOE_STATUS_BAD_INDEX 2u /* moe_permute met an index outside [0, E) (skipped) */
+
+/* ---- layer description --------------------------------------------------- */
+/* [Routing §一] gives the full-size values: E = 256, top_k = 8, n_group = 8,
+ * topk_group = 4, one shared expert, I = 512, routed_scaling_factor = 2.5,
+ * expert bias enabled; hidden size H = 2048.
+ *
+ * Envelope (MOE_ERR_UNSUPPORTED outside it): 2 <= E <= 512; E % n_group == 0;
+ * group size E/n_group >= 2; n_group <= 64; 1 <= top_k <= 16;
+ * top_k <= topk_group * E / n_group; H % 256 == 0 (bf16) or H % 64 == 0 and
+ * H <= 16384 (fp32); I and I_shared multiples of 64 and at most 1024;
+ * T * top_k < 2^31. */
+typedef struct {
+  int32_t T;                   /* tokens */
+  int32_t H;                   /* hidden size */
+  int32_t E;                   /* routed experts */
+  int32_t n_group;             /* expert groups (contiguous index ranges) */
+  int32_t topk_group;          /* groups kept per token */
+  int32_t top_k;               /* experts chosen per token */
+  int32_t I;                   /* routed expert intermediate size */
+  int32_t I_shared;            /* shared expert intermediate size; 0 = no shared expert */
+  float routed_scaling_factor; /* multiplies the normalised weights */
+  int32_t dtype;               /* moe_dtype_t of x, y and all expert weights */
+  uint32_t flags;              /* MOE_F_* */
+} moe_desc_t;
+
+/* Weights.  [Routing §四] stacks each projection of the E experts into one
+ * tensor [E][I][H].  gate/up are used as z_i = sum_h x_h * W[e][i][h]; down,
+ * stored [E][I][H] too, as out_h = sum_i a_i * W_down[e][i][h]. */
+typedef struct {
+  const float* w_router;    /* (device) [E][H] fp32 */
+  const float* expert_bias; /* (device) [E] fp32, or NULL (= zeros) */
+  const void* w_gate;       /* (device) [E][I][H] dtype */
+  const void* w_up;         /* (device) [E][I][H] dtype */
+  const void* w_down;       /* (device) [E][I][H] dtype */
+  const void* ws_gate;      /* (device) [I_shared][H] dtype; NULL iff I_shared == 0 */
+  const void* ws_up;        /* (device) [I_shared][H] dtype */
+  const void* ws_down;      /* (device) [I_shared][H] dtype */
+} moe_weights_t;
+
+/* Bytes of device workspace every entry point below needs for `desc`
+ * (one size covers all of them).  Host only.  Returns 0 on an invalid or
+ * unsupported desc. */
+size_t moe_workspace_size(const moe_desc_t* desc);
+
+/* Router and selection [Routing §二 steps 1-3, §三].
+ *   x           (device) [T][H] dtype
+ *   w_router    (device) [E][H] fp32
+ *   expert_bias (device) [E] fp32 or NULL
+ *   logits      (device) [T][E] fp32, written when non-NULL: the fp32 router
+ *               logits (the bf16 path computes them exactly as
+ *               x . (hi + mid + lo) with W = hi + mid + lo split into three
+ *               bf16 parts, fp32 accumulation)
+ *   topk_idx    (device) [T][top_k] int32, descending biased score
+ *   topk_w      (device) [T][top_k] fp32 routing weights
+ * Tokens with a non-finite logit get topk_idx = 0..top_k-1 and topk_w = 0
+ * (and the status bit when MOE_F_CHECK_FINITE is set). */
+int moe_route(const moe_desc_t* desc, const void* x, const float* w_router,
+              const float* expert_bias, float* logits, int32_t* topk_idx, float* topk_w,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permute by expert [Routing §四 (inference buckets tokens by expert), §六].
+ *   topk_idx    (device) [T][top_k] int32, each in [0, E); an index outside
+ *               that range is skipped (not counted, pair_slot = -1) and sets
+ *               MOE_STATUS_BAD_INDEX
+ *   counts      (device) [E] int32: hits per expert
+ *   offsets     (device) [E+1] int32: exclusive prefix sum, offsets[E] = T*top_k
+ *   sorted_pair (device) [T*top_k] int32: pair ids p = t*top_k + j grouped by
+ *               expert, ascending p inside each expert (stable)
+ *   pair_slot   (device) [T*top_k] int32: inverse, sorted_pair[pair_slot[p]] = p
+ *   tracking    (device) [E] int64 or NULL: tracking[e] += counts[e] */
+int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Experts and combine [Routing §四, §五]:
+ *   y[t] = shared(x[t]) + sum_{j=0..top_k-1} topk_w[t][j] * expert_{e}(x[t])
+ * with e the expert of pair t*top_k + j (from offsets/sorted_pair), the sum
+ * taken in j order in fp32 and rounded once to dtype.  Inputs as produced by
+ * moe_route / moe_permute; y (device) [T][H] dtype, must not alias x.
+ * Hidden activations and per-pair outputs are rounded to dtype between the
+ * projections. */
+int moe_experts(const moe_desc_t* desc, const void* x, const float* topk_w,
+                const int32_t* offsets, const int32_t* sorted_pair, const int32_t* pair_slot,
+                const moe_weights_t* weights, void* y, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* The whole layer: moe_route, moe_permute, moe_experts in sequence.  Every
+ * *_out pointer may be NULL (then the workspace holds it); logits_out is only
+ * written with MOE_F_WRITE_LOGITS.  tracking as in moe_permute. */
+int moe_layer_forward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                      void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                      int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Residual + RMSNorm for stacking layers (not on the pages; gamma = 1):
+ *   x_out = RN(x_in + y)        (skipped, x_out = x_in, when y == NULL)
+ *   r_out = RN(x_out / sqrt(mean(x_out^2) + eps))
+ * all (device) [T][H] dtype, accumulation in fp32.  x_out may equal x_in. */
+int moe_residual_rmsnorm(const moe_desc_t* desc, const void* x_in, const void* y, void* x_out,
+                         void* r_out, float eps, hipStream_t stream);
+
+/* Kernel stages of moe_layer_forward, in launch order (for measurement). */
+typedef enum {
+  MOE_STAGE_ROUTER_SPLIT = 0, /* bf16 only: router weight -> three bf16 parts */
+  MOE_STAGE_LOGITS = 1,
+  MOE_STAGE_SELECT = 2,
+  MOE_STAGE_HIST = 3,
+  MOE_STAGE_SCAN = 4,
+  MOE_STAGE_SCATTER = 5,
+  MOE_STAGE_TILES = 6,
+  MOE_STAGE_GATE_UP = 7,
+  MOE_STAGE_DOWN = 8,
+  MOE_STAGE_COMBINE = 9,
+  MOE_NUM_STAGES = 10
+} moe_stage_t;
+
+/* moe_layer_forward, plus: records `start` on `stream` immediately before the
+ * kernel of `stage` is enqueued and `stop` immediately after, so that
+ * hipEventElapsedTime(start, stop) is that kernel's duration.  Events are
+ * caller-created; nothing else differs from moe_layer_forward.  For
+ * measurement (a stage the desc does not launch records nothing). */
+int moe_layer_forward_timed(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                            void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                            int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
+                            hipStream_t stream, int stage, hipEvent_t start, hipEvent_t stop);
+
+/* Synchronises `stream`, then reads the workspace status word (MOE_STATUS_*)
+ * into *status (host) and clears it. */
+int moe_status(void* ws, size_t ws_bytes, hipStream_t stream, uint32_t* status);
+
+/* The device implementation of sigma32 (see the header comment) applied to
+ * z (device) [n] fp32 -> s (device) [n] fp32.  For verification. */
+int moe_sigmoid32(const float* z, float* s, int64_t n, hipStream_t stream);
+
+/* Static description of an error code. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,146 @@
+"""libmoe's C ABI on the host: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments before any HIP call (so
+these run without a GPU; no test here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from group_limited_top_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["moe_workspace_size", "moe_route", "moe_permute", "moe_experts",
+              "moe_layer_forward", "moe_status", "moe_strerror"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L.LIB, n), n
+    assert set(declared_functions()) == set(L.EXPORTS)
+
+
+def full_desc(L, **kw):
+    base = dict(T=512, H=2048)
+    base.update(kw)
+    T, H = base.pop("T"), base.pop("H")
+    return L.make_desc(T, H, **base)
+
+
+def test_workspace_size(L):
+    d = full_desc(L)
+    n = L.LIB.moe_workspace_size(ctypes.byref(d))
+    T, H, E, K, I = 512, 2048, 256, 8, 512
+    P = T * K
+    # at least the hidden and per-pair outputs of routed + shared rows, in bf16
+    assert n >= 2 * (P * I + T * I + P * H + T * H)
+    assert n < 2 * (P * I + T * I + P * H + T * H) + 16 * 2 ** 20
+    assert n % 256 == 0
+    bigger = L.LIB.moe_workspace_size(ctypes.byref(full_desc(L, T=1024)))
+    assert bigger > n
+    # T = 0 is valid
+    assert L.LIB.moe_workspace_size(ctypes.byref(full_desc(L, T=0))) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=255), -1),                      # E not a multiple of n_group
+    (dict(n_group=256, topk_group=4), -1),  # group size 1
+    (dict(topk_group=9), -1),               # more kept groups than groups
+    (dict(top_k=200), -1),                  # more experts than the kept groups hold
+    (dict(T=-1), -1),
+    (dict(I=0), -1),
+    (dict(E=1024, n_group=8), -2),          # outside the kernels' envelope
+    (dict(H=2000), -2),
+    (dict(I=500), -2),
+    (dict(I=2048), -2),
+    (dict(top_k=17, topk_group=8), -2),
+    (dict(n_group=128, topk_group=4), -2),
+])
+def test_invalid_descs_rejected(L, kw, code):
+    d = full_desc(L, **kw)
+    assert L.LIB.moe_workspace_size(ctypes.byref(d)) == 0
+    rc = L.LIB.moe_route(ctypes.byref(d), None, None, None, None, None, None, None, 0, None)
+    assert rc == code
+    rc = L.LIB.moe_layer_forward(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                                 None, 0, None)
+    assert rc == code
+
+
+def test_bad_flags_and_dtype(L):
+    d = full_desc(L)
+    d.flags = 8
+    assert L.LIB.moe_workspace_size(ctypes.byref(d)) == 0
+    d = full_desc(L)
+    d.dtype = 7
+    assert L.LIB.moe_workspace_size(ctypes.byref(d)) == 0
+    d = full_desc(L)
+    d.routed_scaling_factor = float("nan")
+    assert L.LIB.moe_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_null_and_workspace_errors(L):
+    d = full_desc(L)
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: errors come first
+    # required pointers missing
+    assert L.LIB.moe_route(ctypes.byref(d), None, fake, None, None, fake, fake, fake, 1 << 40,
+                           None) == -1
+    # workspace too small / missing
+    assert L.LIB.moe_route(ctypes.byref(d), fake, fake, None, None, fake, fake, fake, 16,
+                           None) == -3
+    assert L.LIB.moe_route(ctypes.byref(d), fake, fake, None, None, fake, fake, None, 1 << 40,
+                           None) == -3
+    # misaligned pointers
+    odd = ctypes.c_void_p(0x100004)
+    assert L.LIB.moe_route(ctypes.byref(d), odd, fake, None, None, fake, fake, fake, 1 << 40,
+                           None) == -4
+    # y aliasing x
+    W = L.MoeWeights(fake, None, fake, fake, fake, fake, fake, fake)
+    assert L.LIB.moe_layer_forward(ctypes.byref(d), fake, ctypes.byref(W), fake, None, None, None,
+                                   None, None, fake, 1 << 40, None) == -1
+    # shared-expert weights must match I_shared
+    W2 = L.MoeWeights(fake, None, fake, fake, fake, None, None, None)
+    assert L.LIB.moe_layer_forward(ctypes.byref(d), fake, ctypes.byref(W2), ctypes.c_void_p(0x200000),
+                                   None, None, None, None, None, fake, 1 << 40, None) == -1
+    d0 = full_desc(L, I_shared=0)
+    assert L.LIB.moe_layer_forward(ctypes.byref(d0), fake, ctypes.byref(W), ctypes.c_void_p(0x200000),
+                                   None, None, None, None, None, fake, 1 << 40, None) == -1
+
+
+def test_zero_tokens_is_a_noop(L):
+    d = ctypes.byref(full_desc(L, T=0))
+    assert L.LIB.moe_route(d, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.LIB.moe_permute(d, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.LIB.moe_experts(d, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.LIB.moe_layer_forward(d, None, None, None, None, None, None, None, None, None, 0,
+                                   None) == 0
+
+
+def test_strerror(L):
+    for c in [0, -1, -2, -3, -4, -5, 99]:
+        assert isinstance(L.strerror(c), str) and L.strerror(c)
+    assert L.strerror(-3).startswith("workspace")
+
+
+def test_binding_checks_shapes(L):
+    import torch
+    d = full_desc(L, T=4)
+    x = torch.zeros(4, 2048, dtype=torch.bfloat16)  # on the CPU: rejected before any call
+    with pytest.raises(ValueError):
+        L.moe_route(d, x, torch.zeros(256, 2048), None, None, torch.zeros(4, 8, dtype=torch.int32),
+                    torch.zeros(4, 8), torch.zeros(16, dtype=torch.uint8))

@@ -1,0 +1,417 @@
+"""GPU parity of the HIP path (called through the C ABI) against the oracle.
+
+Each case prints what it runs before the GPU step (so a failing run names
+its case).  Bars: indices, counts and permutations bit-exact; fp32 layers
+rel-L2 <= 1e-5, bf16 layers rel-L2 <= 1e-2 (the layer-level tolerances the
+task fixes); routing on random inputs: bit-exact on every token whose choice
+is unique within the logit band (see gpu_helpers.check_routing_random).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_limited_top_amd import synth
+
+from gpu_helpers import (DEV, L, TAU, check_routing_random, gpu_layer, make_layer, nb,
+                         oracle_weights, rel_l2, row_rel, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "routing_hand_examples.json")
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+# --------------------------------------------------------------------------- sigma32
+
+def test_sigmoid32_bit_exact_sampled():
+    """The device sigma32 equals the oracle's on every 251st fp32 bit pattern
+    and on dense runs around the values routing compares."""
+    say("sigmoid32 sampled")
+    bits = np.arange(0, 2 ** 32, 251, dtype=np.uint64).astype(np.uint32)
+    dense = [np.arange(b, b + 2 ** 20, dtype=np.uint32) for b in
+             (0x3F000000, 0xBF000000, 0x40000000, 0xC0000000, 0x42B00000, 0xC2B00000, 0xC2D00000)]
+    z = np.concatenate([bits] + dense).view(np.float32)
+    ref = oracle.sigmoid32(z)
+    zt = torch.from_numpy(z).to(DEV)
+    st = torch.empty_like(zt)
+    L().moe_sigmoid32(zt, st)
+    torch.cuda.synchronize()
+    got = st.cpu().numpy()
+    same = (got.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), f"{(~same).sum()} mismatches, first at z={z[~same][:4]}"
+
+
+# --------------------------------------------------------------------------- routing, exact logits
+
+def _route_exact(lam, bias, n_group, topk_group, top_k, scale, dtype="bf16"):
+    """Route through moe_route with one-hot x, so that every fp32 logit equals
+    lam exactly (a single non-zero product per dot product)."""
+    T, E = lam.shape
+    H = 256 * ((T + 255) // 256)
+    x = torch.zeros(T, H, dtype=torch.float32)
+    x[torch.arange(T), torch.arange(T)] = 1.0
+    wr = torch.zeros(E, H, dtype=torch.float32)
+    wr[:, :T] = torch.from_numpy(lam.T.copy())
+    d = L().make_desc(T, H, E=E, n_group=n_group, topk_group=topk_group, top_k=top_k, I=64,
+                      I_shared=0, scale=scale, dtype=dtype)
+    xt = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32).to(DEV)
+    idx = torch.empty(T, top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, top_k, dtype=torch.float32, device=DEV)
+    lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    ws = L().alloc_workspace(d, DEV)
+    b = None if bias is None else torch.from_numpy(bias).to(DEV)
+    L().moe_route(d, xt, wr.to(DEV), b, lg, idx, w, ws)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ex", _golden(), ids=lambda e: e["name"])
+def test_route_hand_examples(ex, dtype):
+    say("route hand example", ex["name"], dtype)
+    E = ex["E"]
+    if "logits" in ex:
+        lam = np.array([ex["logits"]], np.float32)
+    else:
+        lam = np.full((1, E), ex["logits_default"], np.float32)
+        for k, v in ex["logits_set"].items():
+            lam[0, int(k)] = v
+    bias = None if ex["bias"] is None else np.array(ex["bias"], np.float32)
+    lg, idx, w = _route_exact(lam, bias, ex["n_group"], ex["topk_group"], ex["top_k"],
+                              ex["scale"], dtype)
+    np.testing.assert_array_equal(lg, lam)
+    assert idx[0].tolist() == ex["expected_idx"]
+    ri, rw, _ = oracle.select(lam, bias, ex["n_group"], ex["topk_group"], ex["top_k"], ex["scale"])
+    np.testing.assert_array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["normal", "coarse", "wide", "underflow"])
+@pytest.mark.parametrize("with_bias", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_route_exact_logits_bit_exact(kind, with_bias, dtype):
+    """Random logits (including heavy ties) fed exactly: indices AND weights
+    bit-exact against the oracle's selection."""
+    say("route exact logits", kind, with_bias, dtype)
+    rng = np.random.default_rng(100 + 3 * with_bias + (dtype == "f32"))
+    T, E = 300, 256
+    if kind == "normal":
+        lam = rng.normal(0, 1, (T, E)).astype(np.float32)
+    elif kind == "coarse":
+        lam = (rng.integers(-3, 4, (T, E)) * 0.5).astype(np.float32)
+    elif kind == "wide":
+        lam = rng.normal(0, 8, (T, E)).astype(np.float32)
+    else:  # scores in the subnormal range and exact zeros
+        lam = rng.uniform(-110, -80, (T, E)).astype(np.float32)
+    bias = None
+    if with_bias:
+        bias = (rng.integers(-2, 3, E) * 0.125).astype(np.float32) if kind == "coarse" else \
+            rng.normal(0, 0.05, E).astype(np.float32)
+    lg, idx, w = _route_exact(lam, bias, 8, 4, 8, 2.5, dtype)
+    np.testing.assert_array_equal(lg, lam)
+    ri, rw, rf = oracle.select(lam, bias, 8, 4, 8, 2.5)
+    assert not rf.any()
+    np.testing.assert_array_equal(idx, ri)
+    np.testing.assert_array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(16, 4, 2, 4), (64, 8, 3, 5), (512, 16, 4, 16), (96, 3, 2, 6)])
+def test_route_exact_other_shapes(shape):
+    E, G, KG, K = shape
+    say("route exact other shape", shape)
+    rng = np.random.default_rng(E + G)
+    lam = (rng.integers(-3, 4, (200, E)) * 0.5).astype(np.float32)
+    lg, idx, w = _route_exact(lam, None, G, KG, K, 2.5)
+    ri, rw, _ = oracle.select(lam, None, G, KG, K, 2.5)
+    np.testing.assert_array_equal(idx, ri)
+    np.testing.assert_array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+def test_route_nonfinite_flag():
+    say("route non-finite")
+    Lb = L()
+    rng = np.random.default_rng(7)
+    lam = rng.normal(0, 1, (6, 256)).astype(np.float32)
+    lam[2, 17] = np.nan
+    lam[4, 3] = np.inf
+    T, E, H = 6, 256, 256
+    x = torch.zeros(T, H)
+    x[torch.arange(T), torch.arange(T)] = 1.0
+    wr = torch.zeros(E, H)
+    wr[:, :T] = torch.from_numpy(lam.T.copy())
+    d = Lb.make_desc(T, H, I=64, I_shared=0, flags=Lb.MOE_F_CHECK_FINITE)
+    idx = torch.empty(T, 8, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, 8, dtype=torch.float32, device=DEV)
+    ws = Lb.alloc_workspace(d, DEV)
+    Lb.moe_route(d, x.to(torch.bfloat16).to(DEV), wr.to(DEV), None, None, idx, w, ws)
+    st = Lb.moe_status(ws)
+    assert st & Lb.MOE_STATUS_NONFINITE
+    assert Lb.moe_status(ws) == 0  # cleared by the read
+    gi = idx.cpu().numpy()
+    assert gi.min() >= 0 and gi.max() < E
+    ri, rw, rf = oracle.select(lam, None, 8, 4, 8, 2.5)
+    assert rf.tolist() == [0, 0, 1, 0, 1, 0]
+    ok = rf == 0
+    np.testing.assert_array_equal(gi[ok], ri[ok])
+
+
+# --------------------------------------------------------------------------- routing, random inputs
+
+@pytest.mark.parametrize("name", ["full_t512", "full_t16k_bias"])
+def test_route_random_full_size(name):
+    shape = synth.WORKLOADS[name]
+    say("route random", name)
+    x, wr, b = synth.router_inputs(shape)
+    d = L().desc_from_shape(shape, flags=L().MOE_F_WRITE_LOGITS)
+    T, E = shape.T, shape.E
+    idx = torch.empty(T, 8, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, 8, dtype=torch.float32, device=DEV)
+    lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    ws = L().alloc_workspace(d, DEV)
+    L().moe_route(d, x.to(DEV), wr.to(DEV), None if b is None else b.to(DEV), lg, idx, w, ws)
+    torch.cuda.synchronize()
+    l64 = oracle.logits(nb(x), wr.numpy())
+    dev = {"expert_bias": None if b is None else b}
+    stats = check_routing_random(d, {"expert_bias": None if b is None else b},
+                                 {"logits": lg, "idx": idx, "w": w}, l64)
+    say("route stats", name, stats)
+    assert stats["decided"] >= 0.9 * T
+
+
+# --------------------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("T,kind", [(1, "uniform"), (77, "uniform"), (512, "uniform"),
+                                    (4096, "skew"), (3000, "one_expert"), (16384, "uniform")])
+def test_permute_bit_exact(T, kind):
+    say("permute", T, kind)
+    Lb = L()
+    rng = np.random.default_rng(T)
+    E, K = 256, 8
+    if kind == "uniform":
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    elif kind == "skew":
+        idx = rng.zipf(1.3, (T, K)).astype(np.int64) % E
+        idx = idx.astype(np.int32)
+    else:
+        idx = np.full((T, K), 37, np.int32)
+    d = Lb.make_desc(T, 2048)
+    it = torch.from_numpy(idx).to(DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    sp = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    ps = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    tracking = torch.zeros(E, dtype=torch.int64, device=DEV)
+    ws = Lb.alloc_workspace(d, DEV)
+    for _ in range(2):
+        Lb.moe_permute(d, it, counts, offsets, sp, ps, tracking, ws)
+    torch.cuda.synchronize()
+    c, o, s, p = oracle.permute(idx, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o)
+    np.testing.assert_array_equal(sp.cpu().numpy(), s)
+    np.testing.assert_array_equal(ps.cpu().numpy(), p)
+    np.testing.assert_array_equal(tracking.cpu().numpy(), 2 * c.astype(np.int64))
+    assert Lb.moe_status(ws) == 0
+
+
+# --------------------------------------------------------------------------- experts
+
+def _random_routing(rng, T, E, K):
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.1, 0.6, (T, K)).astype(np.float32)
+    return idx, w
+
+
+def _gpu_experts(d, dev, idx, w):
+    """moe_experts fed with the oracle's permutation of the given routing."""
+    Lb = L()
+    E = d.E
+    c, o, s, p = oracle.permute(idx, E)
+    y = torch.empty(d.T, d.H, dtype=dev["x"].dtype, device=DEV)
+    ws = Lb.alloc_workspace(d, DEV)
+    weights = {k: dev[k] for k in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    Lb.moe_experts(d, dev["x"], torch.from_numpy(w).to(DEV), torch.from_numpy(o).to(DEV),
+                   torch.from_numpy(s).to(DEV), torch.from_numpy(p).to(DEV), weights, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("T,dtype,Is", [(100, "bf16", 64), (100, "bf16", 0), (37, "bf16", 128),
+                                        (100, "f32", 64), (5, "f32", 0), (1, "bf16", 64)])
+def test_experts_small(T, dtype, Is):
+    say("experts small", T, dtype, Is)
+    shape = synth.small_shape(T, H=256, I=64, I_shared=Is, dtype=dtype, seed=300 + T)
+    dev = make_layer(shape)
+    rng = np.random.default_rng(T)
+    idx, w = _random_routing(rng, T, shape.E, shape.top_k)
+    d = L().desc_from_shape(shape)
+    y = _gpu_experts(d, dev, idx, w)
+    ref = oracle.experts(nb(dev["x"]), idx, w, *oracle_weights(dev))
+    got = to_f64(y)
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    assert rel_l2(got, ref) <= tol / 2
+    assert row_rel(got, ref).max() <= tol
+
+
+def test_experts_full_size_sampled_rows():
+    """Full-size shapes (H 2048, I 512), uneven buckets including one expert
+    with many rows: every row of a sample of tokens against the oracle."""
+    shape = synth.WORKLOADS["full_t512"]
+    say("experts full size sampled", shape.T)
+    dev = make_layer(shape)
+    rng = np.random.default_rng(5)
+    idx, w = _random_routing(rng, shape.T, shape.E, shape.top_k)
+    idx[:100, 0] = 5  # expert 5 gets >100 rows: several tiles
+    for t in range(100):
+        if 5 in idx[t, 1:]:
+            idx[t, 1 + list(idx[t, 1:]).index(5)] = 6 if 6 not in idx[t] else 7
+    d = L().desc_from_shape(shape)
+    y = _gpu_experts(d, dev, idx, w)
+    tok = np.array(sorted(set(rng.choice(shape.T, 48, replace=False).tolist()) | {0, 99, 511}),
+                   np.int32)
+    ref = oracle.experts(nb(dev["x"]), idx, w, *oracle_weights(dev), tokens=tok)
+    got = to_f64(y)[tok]
+    assert rel_l2(got, ref) <= 5e-3
+    assert row_rel(got, ref).max() <= 1e-2
+
+
+# --------------------------------------------------------------------------- whole layer
+
+def test_layer_tiny_f32():
+    shape = synth.WORKLOADS["tiny_f32"]
+    say("layer", shape.name)
+    dev = make_layer(shape)
+    d = L().desc_from_shape(shape)
+    gpu = gpu_layer(d, dev)
+    out = oracle.layer(nb(dev["x"]), nb(dev["w_router"]), None, *oracle_weights(dev),
+                       n_group=8, topk_group=4, top_k=8, scale=2.5)
+    stats = check_routing_random(d, dev, gpu, out["l64"], tau=TAU)
+    say("routing", stats)
+    got = to_f64(gpu["y"])
+    assert rel_l2(got, out["y"]) <= 1e-5
+    dec, _ = oracle.route_intervals(out["l64"], TAU, None, 8, 4, 8, out["idx"])
+    ok = (dec & 2) != 0
+    assert row_rel(got[ok], out["y"][ok]).max() <= 1e-5
+
+
+def test_layer_full_t512():
+    shape = synth.WORKLOADS["full_t512"]
+    say("layer", shape.name)
+    dev = make_layer(shape)
+    d = L().desc_from_shape(shape)
+    tracking = torch.zeros(shape.E, dtype=torch.int64, device=DEV)
+    gpu = gpu_layer(d, dev, tracking=tracking)
+    out = oracle.layer(nb(dev["x"]), nb(dev["w_router"]), None, *oracle_weights(dev),
+                       n_group=8, topk_group=4, top_k=8, scale=2.5)
+    stats = check_routing_random(d, dev, gpu, out["l64"])
+    say("routing", stats)
+    got = to_f64(gpu["y"])
+    r = rel_l2(got, out["y"])
+    say("rel_l2", r)
+    assert r <= 1e-2
+    dec, _ = oracle.route_intervals(out["l64"], TAU, None, 8, 4, 8, out["idx"])
+    ok = (dec & 2) != 0
+    assert row_rel(got[ok], out["y"][ok]).max() <= 2e-2
+    # counts: a bincount of the GPU's own indices, and the oracle's where decided
+    gidx = gpu["idx"].cpu().numpy()
+    gc = gpu["counts"].cpu().numpy()
+    np.testing.assert_array_equal(gc, np.bincount(gidx.reshape(-1), minlength=256))
+    oc = np.bincount(out["idx"].reshape(-1), minlength=256)
+    assert np.abs(gc - oc).sum() <= 2 * 8 * int((~ok).sum())
+    np.testing.assert_array_equal(tracking.cpu().numpy(), gc)
+    # determinism: a second call is bit-identical
+    gpu2 = gpu_layer(d, dev, tracking=tracking)
+    assert torch.equal(gpu["y"], gpu2["y"]) and torch.equal(gpu["idx"], gpu2["idx"])
+    assert torch.equal(gpu["w"], gpu2["w"])
+    np.testing.assert_array_equal(tracking.cpu().numpy(), 2 * gc)
+
+
+def test_layer_token_independence():
+    shape = synth.small_shape(64, H=256, I=64, I_shared=64, seed=9)
+    say("layer token independence")
+    dev = make_layer(shape)
+    d = L().desc_from_shape(shape)
+    a = gpu_layer(d, dev)
+    dev2 = dict(dev)
+    dev2["x"] = dev["x"].clone()
+    dev2["x"][10] = -dev2["x"][10]
+    b = gpu_layer(d, dev2)
+    keep = torch.ones(64, dtype=torch.bool)
+    keep[10] = False
+    assert torch.equal(a["y"][keep.to(DEV)], b["y"][keep.to(DEV)])
+    assert not torch.equal(a["y"][10], b["y"][10])
+
+
+@pytest.mark.parametrize("T", [1, 3, 33, 200])
+def test_layer_ragged_small(T):
+    shape = synth.small_shape(T, H=512, I=128, I_shared=64, bias="none", seed=40 + T)
+    say("layer ragged", T)
+    dev = make_layer(shape)
+    d = L().desc_from_shape(shape)
+    gpu = gpu_layer(d, dev)
+    out = oracle.layer(nb(dev["x"]), nb(dev["w_router"]), None, *oracle_weights(dev),
+                       n_group=8, topk_group=4, top_k=8, scale=2.5)
+    check_routing_random(d, dev, gpu, out["l64"])
+    dec, _ = oracle.route_intervals(out["l64"], TAU, None, 8, 4, 8, out["idx"])
+    ok = (dec & 2) != 0
+    got = to_f64(gpu["y"])
+    assert row_rel(got[ok], out["y"][ok]).max() <= 2e-2
+
+
+def test_layer_nonfinite_row_isolated():
+    shape = synth.small_shape(16, H=256, I=64, I_shared=64, seed=11)
+    say("layer non-finite row")
+    Lb = L()
+    dev = make_layer(shape)
+    d = Lb.desc_from_shape(shape, flags=Lb.MOE_F_CHECK_FINITE)
+    a = gpu_layer(d, dev)
+    assert Lb.moe_status(a["ws"]) == 0
+    dev2 = dict(dev)
+    dev2["x"] = dev["x"].clone()
+    dev2["x"][3, 7] = float("nan")
+    b = gpu_layer(d, dev2)
+    assert Lb.moe_status(b["ws"]) & Lb.MOE_STATUS_NONFINITE
+    gi = b["idx"].cpu().numpy()
+    assert gi.min() >= 0 and gi.max() < shape.E
+    keep = torch.ones(16, dtype=torch.bool, device=DEV)
+    keep[3] = False
+    assert torch.equal(a["y"][keep], b["y"][keep])
+
+
+def test_layer_t16k_bias_sampled():
+    shape = synth.WORKLOADS["full_t16k_bias"]
+    say("layer", shape.name)
+    dev = make_layer(shape)
+    d = L().desc_from_shape(shape)
+    gpu = gpu_layer(d, dev)
+    xb = nb(dev["x"])
+    l64 = oracle.logits(xb, nb(dev["w_router"]))
+    stats = check_routing_random(d, dev, gpu, l64)
+    say("routing", stats)
+    bias = nb(dev["expert_bias"])
+    idx, w, _ = oracle.select(l64.astype(np.float32), bias, 8, 4, 8, 2.5)
+    # the bias changes most tokens' choice, the weights stay unbiased
+    idx0, _, _ = oracle.select(l64.astype(np.float32), None, 8, 4, 8, 2.5)
+    assert (np.sort(idx, 1) != np.sort(idx0, 1)).any(1).mean() > 0.5
+    dec, _ = oracle.route_intervals(l64, TAU, bias, 8, 4, 8, idx)
+    rng = np.random.default_rng(3)
+    cand = np.nonzero(dec & 2)[0]
+    tok = np.sort(rng.choice(cand, 192, replace=False)).astype(np.int32)
+    ref = oracle.experts(xb, idx, w, *oracle_weights(dev), tokens=tok)
+    got = to_f64(gpu["y"])[tok]
+    r = rel_l2(got, ref)
+    say("rel_l2 sampled", r)
+    assert r <= 1e-2
+    assert row_rel(got, ref).max() <= 2e-2
