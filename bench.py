@@ -49,6 +49,56 @@ def algorithmic_work(shape, counts):
                 flops_layer=flops_gate_up + flops_down + flops_router)
 
 
+class HipEvents:
+    """Timing events created directly through the HIP runtime, without the
+    system-scope fence torch's events carry (that fence costs several
+    microseconds per record between two kernels)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        try:
+            self.hip = ctypes.CDLL("libamdhip64.so")
+        except OSError:
+            self.hip = ctypes.CDLL("/opt/rocm/lib/libamdhip64.so")
+        self.c = ctypes
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h),
+                                                  ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(h.value)
+
+    def elapsed_ms(self, a, b):
+        ms = self.c.c_float()
+        rc = self.hip.hipEventElapsedTime(self.c.byref(ms), self.c.c_void_p(a), self.c.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(self.c.c_void_p(h))
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter runs
+    (profiles/traffic.json), or None when the kernel sources changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    csrc = os.path.join(ROOT, "group_limited_top_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("experts.hip", "device.h", "kernels.h"))
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(shape, x, wr, bias, w, max_tokens):
     """The oracle as it stands: routing for every token, experts + combine for
     the first `max_tokens` tokens; throughput scaled to tokens/s."""
@@ -86,6 +136,9 @@ def main():
     ap.add_argument("--workload", default="full_t512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times), to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this layer's data-parallel share needs no "
@@ -93,6 +146,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     from group_limited_top_amd import _lib as L
     from group_limited_top_amd import synth
 
@@ -115,29 +178,37 @@ def main():
     ws = L.alloc_workspace(d, dev)
     stage = "gate_up"
     K, W = args.steps, args.warmup
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for a, b in evs:  # create the underlying HIP events before handing them over
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
+    hev = HipEvents(2 * K)
+    pairs = [(hev.ev[2 * i], hev.ev[2 * i + 1]) for i in range(K)]
 
     for _ in range(W):
         L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws)
     torch.cuda.synchronize()
+    # timed region: K steps, each recording an event pair around the dominant
+    # kernel on the library's stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
         L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws, timed_stage=stage,
-                            events=evs[i])
+                            events=pairs[i])
     t_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_stop)
     ms_step = ms_total / K
-    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    kern_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / K
+    hev.close()
+    # the same K steps with no event inside a step, for reference
+    u0 = torch.cuda.Event(enable_timing=True)
+    u1 = torch.cuda.Event(enable_timing=True)
+    u0.record()
+    for i in range(K):
+        L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws)
+    u1.record()
+    torch.cuda.synchronize()
+    ms_step_plain = u0.elapsed_time(u1) / K
     assert L.moe_status(ws) == 0
 
     work = algorithmic_work(shape, counts.cpu().numpy())
@@ -150,7 +221,9 @@ def main():
         achieved = work["k_gate_up"] / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    roof.update(kernel="k_gateup_bf16" if shape.dtype == "bf16" else "k_gateup_f32",
+    kname = "k_gateup_bf16" if shape.dtype == "bf16" else "k_gateup_f32"
+    roof["traffic"] = measured_traffic(shape.name, kname)
+    roof.update(kernel=kname,
                 kernel_ms=round(kern_ms, 4), algorithmic_bytes=work["k_gate_up"],
                 algorithmic_flops=work["flops_gate_up"])
     layer_hbm = work["layer"] / (ms_step * 1e-3) / 1e9
@@ -169,6 +242,7 @@ def main():
                   "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
                   "experts_hit": work["hit"]},
         "wall_s_timed": round(wall, 4),
+        "ms_per_step_no_kernel_events": round(ms_step_plain, 4),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, x, wr, bias, w, args.cpu_tokens)

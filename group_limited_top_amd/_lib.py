@@ -236,7 +236,8 @@ def moe_layer_forward(d: MoeDesc, x, weights: dict, y, topk_idx_out=None, topk_w
                       timed_stage=None, events=None):
     """Whole layer.  With timed_stage (a name from STAGES) and events (a pair
     of torch.cuda.Event(enable_timing=True)), the pair is recorded around that
-    stage's kernel on the same stream (moe_layer_forward_timed)."""
+    stage's kernel on the same stream (moe_layer_forward_timed); raw hipEvent_t
+    handles (ints) are accepted as well."""
     dev = x.device
     T, H, E, K = d.T, d.H, d.E, d.top_k
     dt = _act_dtype(d)
@@ -255,10 +256,10 @@ def moe_layer_forward(d: MoeDesc, x, weights: dict, y, topk_idx_out=None, topk_w
         _rc(LIB.moe_layer_forward(ctypes.byref(d), xp, ctypes.byref(W), *args, p, n,
                                   _stream(stream)), "moe_layer_forward")
         return
-    ev0, ev1 = events
+    ev0, ev1 = (e if isinstance(e, int) else e.cuda_event for e in events)
     _rc(LIB.moe_layer_forward_timed(ctypes.byref(d), xp, ctypes.byref(W), *args, p, n,
                                     _stream(stream), STAGES.index(timed_stage),
-                                    ctypes.c_void_p(ev0.cuda_event), ctypes.c_void_p(ev1.cuda_event)),
+                                    ctypes.c_void_p(ev0), ctypes.c_void_p(ev1)),
         "moe_layer_forward_timed")
 
 

@@ -17,15 +17,15 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // point; regions an entry point does not use are simply left alone.
 struct Layout {
   size_t status;       // uint32 status word (first 256 bytes)
-  size_t split;        // bf16 [3][E][H] router weight parts (bf16 path)
-  size_t logits;       // fp32 [T][E]
+  size_t split;        // bf16 [3][E][H] router weight parts (bf16 path, large T)
+  size_t logits;       // fp32 [ks][T][E] logits (K-split partials when ks > 1)
   size_t idx;          // int32 [T][K]
   size_t w;            // fp32 [T][K]
   size_t counts;       // int32 [E]
   size_t offsets;      // int32 [E+1]
   size_t sorted_pair;  // int32 [P]
   size_t pair_slot;    // int32 [P]
-  size_t chunk_hist;   // int32 [nchunks][E]
+  size_t perm;         // int32 permute scratch (large P only)
   size_t tile_off;     // int32 [E+2]
   size_t h_routed;     // dtype [P][I]
   size_t h_shared;     // dtype [T][Is]
@@ -38,7 +38,8 @@ Layout make_layout(const moe_desc_t& d) {
   const size_t T = (size_t)d.T, H = (size_t)d.H, E = (size_t)d.E, K = (size_t)d.top_k;
   const size_t P = T * K;
   const size_t elt = d.dtype == MOE_BF16 ? 2 : 4;
-  const size_t nchunks = (P + moe::kPermuteChunk - 1) / moe::kPermuteChunk;
+  const bool bf16 = d.dtype == MOE_BF16;
+  const size_t ks = bf16 ? (size_t)moe::logits_ksplit(d.T, d.H, d.E) : 1;
   const size_t Is = (size_t)d.I_shared;
   Layout L;
   size_t o = 0;
@@ -48,15 +49,15 @@ Layout make_layout(const moe_desc_t& d) {
     return at;
   };
   L.status = take(kAlign);
-  L.split = take(d.dtype == MOE_BF16 ? 3 * E * H * 2 : 0);
-  L.logits = take(T * E * 4);
+  L.split = take(bf16 && !moe::logits_split_in_kernel(d.T) ? 3 * E * H * 2 : 0);
+  L.logits = take(ks * T * E * 4);
   L.idx = take(P * 4);
   L.w = take(P * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.sorted_pair = take(P * 4);
   L.pair_slot = take(P * 4);
-  L.chunk_hist = take(nchunks * E * 4);
+  L.perm = take(moe::permute_scratch_ints((int64_t)P, d.E) * 4);
   L.tile_off = take((E + 2) * 4);
   L.h_routed = take(P * (size_t)d.I * elt);
   L.h_shared = take(T * Is * elt);
@@ -81,6 +82,11 @@ int validate(const moe_desc_t* d) {
   if (d->flags & ~(MOE_F_WRITE_LOGITS | MOE_F_CHECK_FINITE)) return MOE_ERR_INVALID;
   // kernel envelope
   if (d->E > 512 || d->n_group > 64 || d->top_k > 16) return MOE_ERR_UNSUPPORTED;
+  {  // the selection kernel maps a group onto a power-of-two run of lanes
+    const int epl = moe::select_epl(d->E);
+    const int lpg = gsize / epl;
+    if (gsize % epl != 0 || (lpg & (lpg - 1)) != 0) return MOE_ERR_UNSUPPORTED;
+  }
   if (d->dtype == MOE_BF16 && d->H % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_F32 && (d->H % 64 != 0 || d->H > 16384)) return MOE_ERR_UNSUPPORTED;
   if (d->I % 64 != 0 || d->I > 1024) return MOE_ERR_UNSUPPORTED;
@@ -104,25 +110,34 @@ int check_ws(const moe_desc_t& d, void* ws, size_t ws_bytes) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// route into (idx, w) with logits in `logits` (never NULL here)
+// route into (idx, w); logits_user (nullable) receives the fp32 logits
 int run_route(const moe_desc_t& d, const void* x, const float* w_router, const float* bias,
-              float* logits, int32_t* idx, float* w, void* ws, hipStream_t s,
+              float* logits_user, int32_t* idx, float* w, void* ws, hipStream_t s,
               const moe::StageTimer* tm = nullptr) {
   const Layout L = make_layout(d);
+  float* part = at<float>(ws, L.logits);
+  int ks = 1;
   hipError_t e;
   if (d.dtype == MOE_BF16) {
-    uint16_t* split = at<uint16_t>(ws, L.split);
-    e = moe::launch_split_router(w_router, split, d.E, d.H, s, tm);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    e = moe::launch_logits_bf16(reinterpret_cast<const uint16_t*>(x), split, logits, d.T, d.H, d.E,
-                                s, tm);
+    ks = moe::logits_ksplit(d.T, d.H, d.E);
+    uint16_t* split = nullptr;
+    if (!moe::logits_split_in_kernel(d.T)) {
+      split = at<uint16_t>(ws, L.split);
+      e = moe::launch_split_router(w_router, split, d.E, d.H, s, tm);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (ks == 1 && logits_user) part = logits_user;
+    e = moe::launch_logits_bf16(reinterpret_cast<const uint16_t*>(x), w_router, split, part, d.T,
+                                d.H, d.E, ks, s, tm);
   } else {
-    e = moe::launch_logits_f32(reinterpret_cast<const float*>(x), w_router, logits, d.T, d.H, d.E,
-                               s, tm);
+    if (logits_user) part = logits_user;
+    e = moe::launch_logits_f32(reinterpret_cast<const float*>(x), w_router, part, d.T, d.H, d.E, s,
+                               tm);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_select(logits, bias, idx, w, at<uint32_t>(ws, L.status), d.T, d.E, d.n_group,
-                         d.topk_group, d.top_k, d.routed_scaling_factor,
+  float* copy_out = (logits_user && part != logits_user) ? logits_user : nullptr;
+  e = moe::launch_select(part, ks, copy_out, bias, idx, w, at<uint32_t>(ws, L.status), d.T, d.E,
+                         d.n_group, d.topk_group, d.top_k, d.routed_scaling_factor,
                          (d.flags & MOE_F_CHECK_FINITE) != 0, s, tm);
   return hip_rc(e);
 }
@@ -131,14 +146,16 @@ int run_permute(const moe_desc_t& d, const int32_t* idx, int32_t* counts, int32_
                 int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking, void* ws,
                 hipStream_t s, const moe::StageTimer* tm = nullptr) {
   const Layout L = make_layout(d);
-  return hip_rc(moe::launch_permute(idx, (int64_t)d.T * d.top_k, d.E, at<int32_t>(ws, L.chunk_hist),
-                                    counts, offsets, sorted_pair, pair_slot, tracking,
+  return hip_rc(moe::launch_permute(idx, (int64_t)d.T * d.top_k, d.E, d.T, d.I_shared,
+                                    at<int32_t>(ws, L.perm), counts, offsets, sorted_pair,
+                                    pair_slot, tracking, at<int32_t>(ws, L.tile_off),
                                     at<uint32_t>(ws, L.status), s, tm));
 }
 
 int run_experts(const moe_desc_t& d, const void* x, const float* topk_w, const int32_t* offsets,
                 const int32_t* sorted_pair, const int32_t* pair_slot, const moe_weights_t& W,
-                void* y, void* ws, hipStream_t s, const moe::StageTimer* tm = nullptr) {
+                void* y, void* ws, hipStream_t s, bool tiles_ready,
+                const moe::StageTimer* tm = nullptr) {
   const Layout L = make_layout(d);
   moe::ExpertArgs a;
   a.T = d.T;
@@ -160,6 +177,7 @@ int run_experts(const moe_desc_t& d, const void* x, const float* topk_w, const i
   a.ws_down = W.ws_down;
   a.y = y;
   a.tile_off = at<int32_t>(ws, L.tile_off);
+  a.tiles_ready = tiles_ready;
   a.h_routed = at<void>(ws, L.h_routed);
   a.h_shared = at<void>(ws, L.h_shared);
   a.o_routed = at<void>(ws, L.o_routed);
@@ -202,8 +220,7 @@ int moe_route(const moe_desc_t* desc, const void* x, const float* w_router,
   const void* ps[] = {x, w_router, expert_bias, logits, topk_idx, topk_w};
   for (const void* p : ps)
     if (misaligned(p)) return MOE_ERR_ALIGN;
-  float* lg = logits ? logits : at<float>(ws, make_layout(*desc).logits);
-  return run_route(*desc, x, w_router, expert_bias, lg, topk_idx, topk_w, ws, stream);
+  return run_route(*desc, x, w_router, expert_bias, logits, topk_idx, topk_w, ws, stream);
 }
 
 int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* counts,
@@ -235,7 +252,8 @@ int moe_experts(const moe_desc_t* desc, const void* x, const float* topk_w,
   const void* ps[] = {x, topk_w, offsets, sorted_pair, pair_slot, y};
   for (const void* p : ps)
     if (misaligned(p)) return MOE_ERR_ALIGN;
-  return run_experts(*desc, x, topk_w, offsets, sorted_pair, pair_slot, *weights, y, ws, stream);
+  return run_experts(*desc, x, topk_w, offsets, sorted_pair, pair_slot, *weights, y, ws, stream,
+                     false);
 }
 
 }  // extern "C"
@@ -255,7 +273,7 @@ static int layer_forward(const moe_desc_t* desc, const void* x, const moe_weight
     if (misaligned(p)) return MOE_ERR_ALIGN;
   const moe_desc_t& d = *desc;
   const Layout L = make_layout(d);
-  float* lg = (logits_out && (d.flags & MOE_F_WRITE_LOGITS)) ? logits_out : at<float>(ws, L.logits);
+  float* lg = (d.flags & MOE_F_WRITE_LOGITS) ? logits_out : nullptr;
   int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
   float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
   int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
@@ -265,7 +283,7 @@ static int layer_forward(const moe_desc_t* desc, const void* x, const moe_weight
   if ((rc = run_route(d, x, weights->w_router, weights->expert_bias, lg, idx, w, ws, stream, tm)))
     return rc;
   if ((rc = run_permute(d, idx, counts, offsets, sp, ps_, tracking, ws, stream, tm))) return rc;
-  return run_experts(d, x, w, offsets, sp, ps_, *weights, y, ws, stream, tm);
+  return run_experts(d, x, w, offsets, sp, ps_, *weights, y, ws, stream, true, tm);
 }
 
 extern "C" {

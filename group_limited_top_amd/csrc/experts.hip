@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_bf16(const ExpertArgs a, int 
   auto load_w = [&](u32x4* g, u32x4* u, int c) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      g[s] = ld16_stream(wg + c * kGuChunk + s * 32);
-      u[s] = ld16_stream(wu + c * kGuChunk + s * 32);
+      g[s] = ld16(wg + c * kGuChunk + s * 32);
+      u[s] = ld16(wu + c * kGuChunk + s * 32);
     }
   };
   auto load_x = [&](int c) {
@@ -335,9 +335,11 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
       reinterpret_cast<const void*>(k_down_bf16), hipFuncAttributeMaxDynamicSharedMemorySize,
       kTileRows * (1024 / 8 + 1) * 16);
   if (attr != hipSuccess) return attr;
-  stage_begin(tm, kTiles, s);
-  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
-  stage_end(tm, kTiles, s);
+  if (!a.tiles_ready) {
+    stage_begin(tm, kTiles, s);
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
+    stage_end(tm, kTiles, s);
+  }
   const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is);
   const int imax = a.I > a.Is ? a.I : a.Is;
   const int slices = imax / 64;
@@ -475,9 +477,11 @@ __global__ __launch_bounds__(256) void k_combine_f32(const ExpertArgs a) {
 }
 
 hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
-  stage_begin(tm, kTiles, s);
-  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
-  stage_end(tm, kTiles, s);
+  if (!a.tiles_ready) {
+    stage_begin(tm, kTiles, s);
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
+    stage_end(tm, kTiles, s);
+  }
   const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is);
   const int imax = a.I > a.Is ? a.I : a.Is;
   const int slices = imax / 64;

@@ -7,6 +7,8 @@
 
 namespace moe {
 
+constexpr int kTileRows = 32;  // token rows per expert tile
+
 // Optional event pair around one kernel stage (see moe_layer_forward_timed).
 struct StageTimer {
   int stage = -1;
@@ -23,25 +25,30 @@ enum Stage { kSplit = 0, kLogits, kSelect, kHist, kScan, kScatter, kTiles, kGate
 // Router ----------------------------------------------------------------------
 hipError_t launch_split_router(const float* w, uint16_t* split, int E, int H, hipStream_t s,
                                const StageTimer* tm = nullptr);
-hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* split, float* logits, int T, int H,
-                              int E, hipStream_t s, const StageTimer* tm = nullptr);
+// K-split factor of the bf16 logits kernel (partials [ks][T][E] are summed by
+// the selection kernel) and whether it splits the router weight itself.
+int logits_ksplit(int T, int H, int E);
+bool logits_split_in_kernel(int T);
+hipError_t launch_logits_bf16(const uint16_t* x, const float* w32, const uint16_t* wsplit,
+                              float* out, int T, int H, int E, int ks, hipStream_t s,
+                              const StageTimer* tm = nullptr);
 hipError_t launch_logits_f32(const float* x, const float* w, float* logits, int T, int H, int E,
                              hipStream_t s, const StageTimer* tm = nullptr);
-hipError_t launch_select(const float* logits, const float* bias, int32_t* idx, float* w,
-                         uint32_t* status, int T, int E, int n_group, int topk_group, int K,
-                         float scale, bool record_nonfinite, hipStream_t s,
+int select_epl(int E);  // experts per lane of the selection kernel (power of two)
+hipError_t launch_select(const float* part, int ks, float* logits_out, const float* bias,
+                         int32_t* idx, float* w, uint32_t* status, int T, int E, int n_group,
+                         int topk_group, int K, float scale, bool record_nonfinite, hipStream_t s,
                          const StageTimer* tm = nullptr);
 hipError_t launch_sigmoid32(const float* z, float* out, int64_t n, hipStream_t s);
 
 // Permute ---------------------------------------------------------------------
-constexpr int kPermuteChunk = 1024;  // pairs per histogram / scatter block
-hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* chunk_hist,
+size_t permute_scratch_ints(int64_t P, int E);
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int32_t* scratch,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                          int32_t* pair_slot, int64_t* tracking, uint32_t* status,
-                          hipStream_t s, const StageTimer* tm = nullptr);
+                          int32_t* pair_slot, int64_t* tracking, int32_t* tile_off,
+                          uint32_t* status, hipStream_t s, const StageTimer* tm = nullptr);
 
 // Experts ---------------------------------------------------------------------
-constexpr int kTileRows = 32;  // token rows per expert tile
 
 struct ExpertArgs {
   int T, H, E, K, I, Is;
@@ -55,6 +62,7 @@ struct ExpertArgs {
   void* y;
   // workspace
   int32_t* tile_off;  // [E+2]
+  bool tiles_ready;   // tile_off already built (by the permute kernels)
   void* h_routed;     // [P][I]
   void* h_shared;     // [T][Is]
   void* o_routed;     // [P][H]

@@ -2,16 +2,20 @@
 //
 // [Routing §六]: per-expert hit counts are a bincount of the chosen indices;
 // [Routing §四]: the eager inference path sorts tokens into one bucket per
-// expert before running each bucket.  Here the T*K (token, slot) pairs,
-// p = t*K + j, are counting-sorted by expert, keeping ascending p inside each
-// bucket, in three deterministic kernels (integer LDS atomics only):
-//   1. per-chunk histograms (chunks of kPermuteChunk consecutive pairs);
-//   2. one block: per-expert scan over chunks, counts, exclusive offsets,
-//      tracking += counts;
-//   3. per chunk, one wave walks its pairs in order and scatters them, ranking
-//      equal experts inside each 64-pair step with ballots.
-// An index outside [0, E) is skipped (not counted, pair_slot = -1) and raises
-// status bit 2 in the workspace status word.
+// expert before running each bucket.  The T*K (token, slot) pairs
+// p = t*K + j are counting-sorted by expert keeping ascending p inside each
+// bucket.  Ranks are computed without atomics on the data path: a wave takes 64
+// consecutive pairs at a time, finds the lanes holding the same expert with
+// ballots over the index bits, and ranks each lane among the lower lanes of
+// its group; per-wave running counts live in LDS.  Everything is integer
+// arithmetic in a fixed order, so results are deterministic.
+//
+// The same kernels also build the expert-tile list (tile_off, kTileRows rows
+// per tile; the shared expert is "expert" E with T rows) used by the expert
+// kernels.
+//
+// An index outside [0, E) is skipped (not counted, pair_slot = -1) and sets
+// status bit 2.
 #include "device.h"
 #include "kernels.h"
 
@@ -19,114 +23,274 @@ namespace moe {
 
 constexpr int kPermMaxE = 512;
 
-__global__ __launch_bounds__(256) void k_chunk_hist(const int32_t* __restrict__ idx, int64_t P,
-                                                     int E, int32_t* __restrict__ chunk_hist) {
-  __shared__ int32_t hist[kPermMaxE];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
-  const int64_t p0 = (int64_t)blockIdx.x * kPermuteChunk;
-  const int64_t p1 = min(P, p0 + kPermuteChunk);
-  for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-    const int32_t e = idx[p];
-    if ((uint32_t)e < (uint32_t)E) atomicAdd(&hist[e], 1);
+// Ballot-based match: `same` = lanes holding the same valid expert as this one.
+__device__ __forceinline__ uint64_t match_lanes(int32_t e, bool valid, int nbits) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    same &= bit ? ones : ~ones;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    chunk_hist[(size_t)blockIdx.x * E + e] = hist[e];
+  return same;
 }
 
-// One block of kPermMaxE threads (thread e owns expert e).
-__global__ __launch_bounds__(kPermMaxE) void k_count_scan(int32_t* __restrict__ chunk_hist,
-                                                          int nchunks, int E, int64_t P,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int64_t* __restrict__ tracking) {
-  __shared__ int32_t scan[kPermMaxE];
-  const int e = threadIdx.x;
-  int32_t total = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int32_t v = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = total;  // exclusive prefix over chunks
-      total += v;
-    }
+// Inclusive scan of v over the block's 1024 threads: shuffle scan inside each
+// wave, then the 16 wave totals.
+__device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t o = __shfl_up(v, d);
+    if (lane >= d) v += o;
   }
-  scan[e] = total;
+  if (lane == 63) sc[w] = v;
   __syncthreads();
-  // inclusive Hillis-Steele scan over experts
-  for (int d = 1; d < kPermMaxE; d <<= 1) {
-    const int32_t add = (e >= d) ? scan[e - d] : 0;
-    __syncthreads();
-    scan[e] += add;
-    __syncthreads();
+  if (w == 0) {
+    int32_t t = lane < 16 ? sc[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int32_t o = __shfl_up(t, d);
+      if (lane >= d) t += o;
+    }
+    if (lane < 16) sc[16 + lane] = t;
   }
-  const int32_t excl = scan[e] - total;
+  __syncthreads();
+  const int32_t r = v + (w > 0 ? sc[16 + w - 1] : 0);
+  __syncthreads();
+  return r;
+}
+
+// counts/offsets/tracking/tile_off from per-expert totals held by thread e.
+__device__ __forceinline__ void finish_counts(int32_t total, int E, int T, int Is, int32_t* sc,
+                                              int32_t* counts, int32_t* offsets,
+                                              int32_t* offs_lds, int64_t* tracking,
+                                              int32_t* tile_off) {
+  const int e = threadIdx.x;
+  const int32_t incl = block_scan_1024(e < E ? total : 0, sc);
   if (e < E) {
     counts[e] = total;
-    offsets[e] = excl;
+    offsets[e] = incl - total;
+    if (offs_lds) offs_lds[e] = incl - total;
     if (tracking) tracking[e] += (int64_t)total;
-    for (int c = 0; c < nchunks; ++c) chunk_hist[(size_t)c * E + e] += excl;
   }
-  if (e == E - 1) offsets[E] = excl + total;
+  if (e == E - 1) offsets[E] = incl;
+  // tiles of kTileRows rows per expert, the shared expert last
+  int32_t n = 0;
+  if (e < E) n = (total + kTileRows - 1) / kTileRows;
+  else if (e == E && Is > 0) n = (T + kTileRows - 1) / kTileRows;
+  const int32_t tin = block_scan_1024(n, sc);
+  if (e <= E) tile_off[e] = tin - n;
+  if (e == E) tile_off[E + 1] = tin;
 }
 
-__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ idx, int64_t P, int E,
-                                                const int32_t* __restrict__ chunk_base,
-                                                int32_t* __restrict__ sorted_pair,
-                                                int32_t* __restrict__ pair_slot,
-                                                uint32_t* __restrict__ status) {
-  __shared__ int32_t cursor[kPermMaxE];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cursor[e] = chunk_base[(size_t)blockIdx.x * E + e];
+// ----------------------------------------------------------------------------
+// Small P (<= 16 waves x 16 batches x 64 = 16384 pairs): one block does it all.
+// ----------------------------------------------------------------------------
+constexpr int kSmallWaves = 16, kSmallBatches = 16;
+constexpr int kSmallMaxP = kSmallWaves * kSmallBatches * 64;
+
+__global__ __launch_bounds__(1024) void k_permute_small(
+    const int32_t* __restrict__ idx, int P, int E, int T, int Is, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_slot, int64_t* __restrict__ tracking,
+    int32_t* __restrict__ tile_off, uint32_t* __restrict__ status) {
+  __shared__ int32_t cnt[kSmallWaves][kPermMaxE];  // 32 KB
+  __shared__ int32_t sc[1024];
+  __shared__ int32_t offs[kPermMaxE];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kSmallWaves * kPermMaxE; i += 1024) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const int nbits = 32 - __clz(E - 1);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t p0 = (int64_t)blockIdx.x * kPermuteChunk;
-  const int64_t p1 = min(P, p0 + kPermuteChunk);
+  const int per = ((P + kSmallWaves * 64 - 1) / (kSmallWaves * 64)) * 64;  // pairs per wave
+  const int p0 = w * per;
+  int32_t rank[kSmallBatches], ev[kSmallBatches];
   int bad = 0;
-  for (int64_t base = p0; base < p1; base += 64) {
-    const int64_t p = base + lane;
-    const bool active = p < p1;
-    const int32_t e = active ? idx[p] : 0;
-    const bool valid = active && (uint32_t)e < (uint32_t)E;
-    bad |= active && !valid;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const uint64_t ones = __ballot(valid && ((e >> b) & 1));
-      same &= ((e >> b) & 1) ? ones : ~ones;
+#pragma unroll
+  for (int b = 0; b < kSmallBatches; ++b) {
+    rank[b] = -1;
+    ev[b] = -1;
+    if (b * 64 < per) {  // block-uniform
+      const int p = p0 + b * 64 + lane;
+      const bool active = p < P && b * 64 + lane < per;
+      const int32_t e = active ? idx[p] : 0;
+      const bool valid = active && (uint32_t)e < (uint32_t)E;
+      bad |= active && !valid;
+      const uint64_t same = match_lanes(e, valid, nbits);
+      if (valid) {
+        const int32_t old = cnt[w][e];
+        rank[b] = old + __popcll(same & below);
+        ev[b] = e;
+        if ((same >> lane) == 1ull) cnt[w][e] = old + __popcll(same);  // last lane of its group
+      }
     }
-    int32_t pos = -1;
-    if (valid) pos = cursor[e] + __popcll(same & below);
-    __syncthreads();  // every lane has read its cursor before any update
-    if (valid && (same >> lane) == 1ull) cursor[e] += __popcll(same);  // last lane of its group
-    if (valid) sorted_pair[pos] = (int32_t)p;
-    if (active) pair_slot[p] = pos;
-    __syncthreads();
+  }
+  __syncthreads();
+  // exclusive prefix over waves for each expert; totals
+  int32_t total = 0;
+  if (threadIdx.x < E) {
+    for (int ww = 0; ww < kSmallWaves; ++ww) {
+      const int32_t c = cnt[ww][threadIdx.x];
+      cnt[ww][threadIdx.x] = total;
+      total += c;
+    }
+  }
+  finish_counts(total, E, T, Is, sc, counts, offsets, offs, tracking, tile_off);
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < kSmallBatches; ++b) {
+    if (b * 64 < per) {
+      const int p = p0 + b * 64 + lane;
+      if (p < P && b * 64 + lane < per) {
+        const int32_t e = ev[b];
+        int32_t pos = -1;
+        if (e >= 0) {
+          pos = offs[e] + cnt[w][e] + rank[b];
+          sorted_pair[pos] = p;
+        }
+        pair_slot[p] = pos;
+      }
+    }
   }
   if (__any(bad) && lane == 0) atomicOr(status, 2u);
 }
 
-hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* chunk_hist,
+// ----------------------------------------------------------------------------
+// Large P: rank per chunk -> one-block scan (+ tiles) -> scatter.
+// A chunk of `ch` pairs is split over the 4 waves of a block; ch is a power of
+// two >= 1024 chosen so that there are at most 64 chunks.
+// ----------------------------------------------------------------------------
+int permute_chunk(int64_t P) {
+  int64_t ch = 1024;
+  while ((P + ch - 1) / ch > 64) ch *= 2;
+  return (int)ch;
+}
+
+__global__ __launch_bounds__(256) void k_perm_rank(const int32_t* __restrict__ idx, int64_t P,
+                                                    int E, int ch, int32_t* __restrict__ prank,
+                                                    int32_t* __restrict__ chunk_hist,
+                                                    uint32_t* __restrict__ status) {
+  __shared__ int32_t cnt[4][kPermMaxE];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * kPermMaxE; i += 256) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int nbits = 32 - __clz(E - 1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int sub = ch / 4;
+  const int64_t q0 = (int64_t)blockIdx.x * ch + (int64_t)w * sub;
+  int bad = 0;
+  for (int b = 0; b < sub; b += 64) {
+    const int64_t p = q0 + b + lane;
+    const bool active = p < P;
+    const int32_t e = active ? idx[p] : 0;
+    const bool valid = active && (uint32_t)e < (uint32_t)E;
+    bad |= active && !valid;
+    const uint64_t same = match_lanes(e, valid, nbits);
+    if (valid) {
+      const int32_t old = cnt[w][e];
+      prank[p] = old + __popcll(same & below);
+      if ((same >> lane) == 1ull) cnt[w][e] = old + __popcll(same);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int32_t run = 0;
+    for (int ww = 0; ww < 4; ++ww) {
+      const int32_t c = cnt[ww][e];
+      cnt[ww][e] = run;
+      run += c;
+    }
+    chunk_hist[(size_t)blockIdx.x * E + e] = run;
+  }
+  __syncthreads();
+  // add the wave's prefix inside the chunk
+  for (int b = 0; b < sub; b += 64) {
+    const int64_t p = q0 + b + lane;
+    if (p < P) {
+      const int32_t e = idx[p];
+      if ((uint32_t)e < (uint32_t)E) prank[p] += cnt[w][e];
+    }
+  }
+  if (__any(bad) && lane == 0) atomicOr(status, 2u);
+}
+
+__global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ chunk_hist,
+                                                     int nchunks, int E, int T, int Is,
+                                                     int32_t* __restrict__ chunk_base,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int64_t* __restrict__ tracking,
+                                                     int32_t* __restrict__ tile_off) {
+  __shared__ int32_t sc[1024];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < E) {
+    for (int c0 = 0; c0 < nchunks; c0 += 16) {
+      int32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nchunks) ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < nchunks) chunk_base[(size_t)(c0 + i) * E + e] = total;
+        total += v[i];
+      }
+    }
+  }
+  finish_counts(total, E, T, Is, sc, counts, offsets, nullptr, tracking, tile_off);
+}
+
+__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ idx, int64_t P,
+                                                       int E, int ch,
+                                                       const int32_t* __restrict__ prank,
+                                                       const int32_t* __restrict__ chunk_base,
+                                                       const int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted_pair,
+                                                       int32_t* __restrict__ pair_slot) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= P) return;
+  const int32_t e = idx[p];
+  int32_t pos = -1;
+  if ((uint32_t)e < (uint32_t)E) {
+    pos = offsets[e] + chunk_base[(size_t)(p / ch) * E + e] + prank[p];
+    sorted_pair[pos] = (int32_t)p;
+  }
+  pair_slot[p] = pos;
+}
+
+size_t permute_scratch_ints(int64_t P, int E) {
+  if (P <= kSmallMaxP) return 0;
+  const int64_t nch = (P + permute_chunk(P) - 1) / permute_chunk(P);
+  return (size_t)P + 2 * (size_t)nch * E;  // prank, chunk_hist, chunk_base
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int32_t* scratch,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                          int32_t* pair_slot, int64_t* tracking, uint32_t* status,
-                          hipStream_t s, const StageTimer* tm) {
-  const int nchunks = (int)((P + kPermuteChunk - 1) / kPermuteChunk);
-  if (nchunks > 0) {
+                          int32_t* pair_slot, int64_t* tracking, int32_t* tile_off,
+                          uint32_t* status, hipStream_t s, const StageTimer* tm) {
+  if (P <= kSmallMaxP) {
     stage_begin(tm, kHist, s);
-    hipLaunchKernelGGL(k_chunk_hist, dim3((unsigned)nchunks), dim3(256), 0, s, idx, P, E,
-                       chunk_hist);
+    hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, s, idx, (int)P, E, T, Is, counts,
+                       offsets, sorted_pair, pair_slot, tracking, tile_off, status);
     stage_end(tm, kHist, s);
+    return hipGetLastError();
   }
+  const int ch = permute_chunk(P);
+  const int nch = (int)((P + ch - 1) / ch);
+  int32_t* prank = scratch;
+  int32_t* chunk_hist = scratch + P;
+  int32_t* chunk_base = chunk_hist + (size_t)nch * E;
+  stage_begin(tm, kHist, s);
+  hipLaunchKernelGGL(k_perm_rank, dim3((unsigned)nch), dim3(256), 0, s, idx, P, E, ch, prank,
+                     chunk_hist, status);
+  stage_end(tm, kHist, s);
   stage_begin(tm, kScan, s);
-  hipLaunchKernelGGL(k_count_scan, dim3(1), dim3(kPermMaxE), 0, s, chunk_hist, nchunks, E, P,
-                     counts, offsets, tracking);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E, T, Is, chunk_base,
+                     counts, offsets, tracking, tile_off);
   stage_end(tm, kScan, s);
-  if (nchunks > 0) {
-    stage_begin(tm, kScatter, s);
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)nchunks), dim3(64), 0, s, idx, P, E, chunk_hist,
-                       sorted_pair, pair_slot, status);
-    stage_end(tm, kScatter, s);
-  }
+  stage_begin(tm, kScatter, s);
+  hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, idx, P, E,
+                     ch, prank, chunk_base, offsets, sorted_pair, pair_slot);
+  stage_end(tm, kScatter, s);
   return hipGetLastError();
 }
 

@@ -98,50 +98,156 @@ hipError_t launch_split_router(const float* w, uint16_t* split, int E, int H, hi
 
 // ----------------------------------------------------------------------------
 // Logits, bf16 activations: logits[t][e] = sum_h x[t][h] * w[e][h] on MFMA with
-// w split three ways (hi, mid, lo).  Block = 4 waves; block tile 16 tokens x
-// 64 experts, each wave 16 x 16.  [Routing §二 step 1]: linear layer in fp32,
-// no bias term.
+// w = hi + mid + lo (three bf16 parts), fp32 accumulation.  [Routing §二 step
+// 1]: a linear layer in fp32 with no bias term.
+//
+// Block: 4 waves, tile 64 tokens (16 per wave) x 64 experts (4 MFMA N-tiles),
+// K range [z*KR, (z+1)*KR) with z = blockIdx.z (a K split for small T; the
+// partial sums are added in fixed order by the selection kernel).  The weight
+// tile of each 64-deep K chunk is staged in LDS as three bf16 planes, split
+// from fp32 inside the kernel (SPLIT, small T: each element is split by at
+// most a few blocks) or copied from the pre-split planes (large T).  x rows go
+// straight from global memory into the A operands.
 // ----------------------------------------------------------------------------
+constexpr int kLgBM = 64, kLgBN = 64, kLgKC = 64, kLgRow = kLgKC + 8;  // +8: bank spread
+constexpr int kMaxKSplit = 16;
+
+__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_bits(v);
+  const float r1 = v - bf16_to_f32((uint16_t)hi);
+  mid = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_to_f32((uint16_t)mid);
+  lo = f32_to_bf16_bits(r2);
+}
+
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ split,
-                                                      float* __restrict__ logits, int T, int H,
-                                                      int E) {
+                                                      const float* __restrict__ w32,
+                                                      const uint16_t* __restrict__ wsplit,
+                                                      float* __restrict__ out, int T, int H,
+                                                      int E, int KR) {
+  __shared__ uint16_t wl[2][3][kLgBN][kLgRow];  // 55 KB
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int t0 = blockIdx.x * 16;
-  const int e0 = blockIdx.y * 64 + wave * 16;
-  if (e0 >= E) return;  // wave-uniform; this kernel has no barrier
-  const int ta = min(t0 + r, T - 1);
-  const int eb = min(e0 + r, E - 1);
-  const size_t EH = (size_t)E * H;
-  const uint16_t* xa = x + (size_t)ta * H + q * 8;
-  const uint16_t* wb = split + (size_t)eb * H + q * 8;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < H; k += 32) {
-    const u32x4 a = ld16(xa + k);
-    const u32x4 b0 = ld16(wb + k);
-    const u32x4 b1 = ld16(wb + EH + k);
-    const u32x4 b2 = ld16(wb + 2 * EH + k);
-    acc = mfma16x16x32(a, b0, acc);
-    acc = mfma16x16x32(a, b1, acc);
-    acc = mfma16x16x32(a, b2, acc);
-  }
-  // C rows are tokens (A), columns experts (B): lane holds C[4q + i][r]
-  const int e = e0 + r;
-  if (e < E) {
+  const int t0 = blockIdx.x * kLgBM, e0 = blockIdx.y * kLgBN, kbeg = blockIdx.z * KR;
+  // staging role: expert row er, 16 consecutive k at ks16
+  const int er = threadIdx.x >> 2, ks16 = (threadIdx.x & 3) * 16;
+  const int erc = min(e0 + er, E - 1);
+  const float* wsrc32 = SPLIT ? w32 + (size_t)erc * H + kbeg + ks16 : nullptr;
+  const uint16_t* wsrc16 = SPLIT ? nullptr : wsplit + (size_t)erc * H + kbeg + ks16;
+  const size_t plane = (size_t)E * H;
+  const int ta = min(t0 + wave * 16 + r, T - 1);
+  const uint16_t* xa = x + (size_t)ta * H + kbeg + q * 8;
+
+  u32x4 st[6];  // staged global data: 16 fp32 (SPLIT) or 3 x 16 bf16
+  auto load_w = [&](int c) {
+    if (SPLIT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * q + i;
-      if (t < T) logits[(size_t)t * E + e] = acc[i];
+      for (int i = 0; i < 4; ++i) st[i] = ld16(wsrc32 + c * kLgKC + 4 * i);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        st[2 * p] = ld16(wsrc16 + p * plane + c * kLgKC);
+        st[2 * p + 1] = ld16(wsrc16 + p * plane + c * kLgKC + 8);
+      }
+    }
+  };
+  auto store_w = [&](int buf) {
+    u32x4 o[6];
+    if (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {  // 8 pairs of fp32 -> 3 packed bf16 pairs
+        const float a = __uint_as_float(st[i >> 1][(i & 1) * 2]);
+        const float b = __uint_as_float(st[i >> 1][(i & 1) * 2 + 1]);
+        uint32_t ah, am, al, bh, bm, bl;
+        split3(a, ah, am, al);
+        split3(b, bh, bm, bl);
+        o[0 + (i >> 2)][i & 3] = ah | (bh << 16);
+        o[2 + (i >> 2)][i & 3] = am | (bm << 16);
+        o[4 + (i >> 2)][i & 3] = al | (bl << 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) o[i] = st[i];
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      st16(&wl[buf][p][er][ks16], o[2 * p]);
+      st16(&wl[buf][p][er][ks16 + 8], o[2 * p + 1]);
+    }
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nchunks = KR / kLgKC;
+  u32x4 a_cur[2], a_nxt[2];
+  load_w(0);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) a_cur[s] = ld16(xa + s * 32);
+  store_w(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunks;
+    if (more) {
+      load_w(c + 1);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) a_nxt[s] = ld16(xa + (c + 1) * kLgKC + s * 32);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(&wl[buf][p][n * 16 + r][s * 32 + q * 8]);
+          acc[n] = mfma16x16x32(a_cur[s], b, acc[n]);
+        }
+      }
+    }
+    if (more) {
+      store_w(buf ^ 1);
+      a_cur[0] = a_nxt[0];
+      a_cur[1] = a_nxt[1];
+    }
+    __syncthreads();
+  }
+  // lane holds C[token 4q + i][expert r] of N-tile n
+  float* o = out + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int e = e0 + n * 16 + r;
+    if (e < E) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wave * 16 + 4 * q + i;
+        if (t < T) o[(size_t)t * E + e] = acc[n][i];
+      }
     }
   }
 }
 
-hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* split, float* logits, int T, int H,
-                              int E, hipStream_t s, const StageTimer* tm) {
-  dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 63) / 64));
+int logits_ksplit(int T, int H, int E) {
+  const int tiles = ((T + kLgBM - 1) / kLgBM) * ((E + kLgBN - 1) / kLgBN);
+  int ks = 1;
+  while (ks < kMaxKSplit && tiles * ks * 2 <= 512 && (H / kLgKC) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+bool logits_split_in_kernel(int T) { return T <= 1024; }
+
+hipError_t launch_logits_bf16(const uint16_t* x, const float* w32, const uint16_t* wsplit,
+                              float* out, int T, int H, int E, int ks, hipStream_t s,
+                              const StageTimer* tm) {
+  dim3 grid((unsigned)((T + kLgBM - 1) / kLgBM), (unsigned)((E + kLgBN - 1) / kLgBN), (unsigned)ks);
+  const int KR = H / ks;
   stage_begin(tm, kLogits, s);
-  hipLaunchKernelGGL(k_logits_bf16, grid, dim3(256), 0, s, x, split, logits, T, H, E);
+  if (logits_split_in_kernel(T))
+    hipLaunchKernelGGL(k_logits_bf16<true>, grid, dim3(256), 0, s, x, w32, wsplit, out, T, H, E, KR);
+  else
+    hipLaunchKernelGGL(k_logits_bf16<false>, grid, dim3(256), 0, s, x, w32, wsplit, out, T, H, E,
+                       KR);
   stage_end(tm, kLogits, s);
   return hipGetLastError();
 }
@@ -181,43 +287,110 @@ hipError_t launch_logits_f32(const float* x, const float* w, float* logits, int 
 }
 
 // ----------------------------------------------------------------------------
-// Selection.  One 64-lane block per token.
-//   [Routing §二 step 1]  s = sigma32(logit) per expert
-//   [Routing §三]         sb = s + bias (selection only)
-//   [Routing §二 step 2]  groups = contiguous ranges of E/n_group experts; group
-//                         score = sum of its two largest sb; keep topk_group
-//                         groups (ties: lower group); others masked to -inf;
-//                         top_k of the rest by (sb desc, expert asc)
-//   [Routing §二 step 3]  w_j = RN(RN(s_j / RN(S + 1e-20)) * scale), S the fp32
-//                         sum of the chosen unbiased scores in choice order
+// Selection.  One wave per token (4 tokens per block); lane l holds the EPL
+// consecutive experts l*EPL .. l*EPL+EPL-1, so a group of E/n_group experts is
+// LPG = E/(n_group*EPL) consecutive lanes.
+//   [Routing §二 step 1]  s = sigma32(logit) (logit = the K-split partials added
+//                         in split order)
+//   [Routing §三]         sb = s + bias, used for selection only
+//   [Routing §二 step 2]  group score = sum of the group's two largest sb
+//                         (xor butterfly over the group's lanes); a group is
+//                         kept when fewer than topk_group groups rank before
+//                         it (higher score, or equal score and lower index);
+//                         the others are masked to -inf; then top_k rounds of
+//                         a wave-wide maximum of 64-bit keys (orderable sb,
+//                         then the complement of the expert index, so that
+//                         ties go to the lower index), by DPP within 16-lane
+//                         rows and readlane across rows
+//   [Routing §二 step 3]  S = fp32 sum of the chosen unbiased scores in choice
+//                         order, w_j = RN(RN(s_j / RN(S + 1e-20)) * scale)
 // ----------------------------------------------------------------------------
-constexpr int kMaxE = 512;
-constexpr int kMaxTopK = 16;
+__device__ __forceinline__ uint32_t orderable(float v) {
+  const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);  // -0 ranks as +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
-__global__ __launch_bounds__(64) void k_select(const float* __restrict__ logits,
-                                                const float* __restrict__ bias,
-                                                int32_t* __restrict__ idx, float* __restrict__ wout,
-                                                uint32_t* __restrict__ status, int E, int n_group,
-                                                int topk_group, int K, float scale, int record) {
-  __shared__ float s_s[kMaxE];
-  __shared__ float s_sb[kMaxE];
-  __shared__ float s_gs[64];
-  __shared__ int s_keep[64];
-  __shared__ int s_sel[kMaxTopK];
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* lg = logits + (size_t)t * E;
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the 64 lanes, returned in every lane.  All lanes must be active.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o = dpp_u64<0xB1>(v);  // quad_perm [1,0,3,2]
+  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);  // quad_perm [2,3,0,1]
+  v = o > v ? o : v;
+  o = dpp_u64<0x141>(v);  // row_half_mirror
+  v = o > v ? o : v;
+  o = dpp_u64<0x140>(v);  // row_mirror: every lane holds its 16-lane row maximum
+  v = o > v ? o : v;
+  uint64_t m = readlane_u64(v, 0);
+  uint64_t m1 = readlane_u64(v, 16);
+  m = m1 > m ? m1 : m;
+  m1 = readlane_u64(v, 32);
+  m = m1 > m ? m1 : m;
+  m1 = readlane_u64(v, 48);
+  return m1 > m ? m1 : m;
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, int KS,
+                                                 float* __restrict__ logits_out,
+                                                 const float* __restrict__ bias,
+                                                 int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                 uint32_t* __restrict__ status, int T, int E,
+                                                 int n_group, int topk_group, int K, float scale,
+                                                 int record) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform; no barrier in this kernel
+  float z[EPL], s[EPL], sb[EPL];
+  bool valid[EPL];
   int bad = 0;
-  for (int e = lane; e < E; e += 64) {
-    const float z = lg[e];
-    const float s = sigmoid32(z);
-    const float sb = s + (bias ? bias[e] : 0.0f);
-    bad |= !(__builtin_isfinite(z) && __builtin_isfinite(sb));
-    s_s[e] = s;
-    s_sb[e] = sb;
+  // issue every partial-sum load first, then add them in split order
+  float pv[kMaxKSplit][EPL];
+#pragma unroll
+  for (int k = 0; k < kMaxKSplit; ++k) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane * EPL + i;
+      pv[k][i] = (k < KS && e < E) ? part[((size_t)k * T + t) * E + e] : 0.0f;
+    }
   }
-  if (__any(bad)) {  // block-uniform: the block is one wave
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    valid[i] = lane * EPL + i < E;
+    float acc = pv[0][i];
+#pragma unroll
+    for (int k = 1; k < kMaxKSplit; ++k)
+      if (k < KS) acc = acc + pv[k][i];
+    z[i] = acc;
+  }
+  if (logits_out) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (valid[i]) logits_out[(size_t)t * E + lane * EPL + i] = z[i];
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    s[i] = sigmoid32(z[i]);
+    sb[i] = s[i] + ((bias && valid[i]) ? bias[lane * EPL + i] : 0.0f);
+    bad |= valid[i] && !(__builtin_isfinite(z[i]) && __builtin_isfinite(sb[i]));
+  }
+  if (__any(bad)) {
     if (lane < K) {
       idx[(size_t)t * K + lane] = lane;
       wout[(size_t)t * K + lane] = 0.0f;
@@ -225,93 +398,105 @@ __global__ __launch_bounds__(64) void k_select(const float* __restrict__ logits,
     if (lane == 0 && record) atomicOr(status, 1u);
     return;
   }
-  __syncthreads();
-
-  const int gsize = E / n_group;
-  if (lane < n_group) {
-    float m1 = -INFINITY, m2 = -INFINITY;
-    const float* g = s_sb + lane * gsize;
-    for (int i = 0; i < gsize; ++i) {
-      const float v = g[i];
-      if (v > m1) {
-        m2 = m1;
-        m1 = v;
-      } else if (v > m2) {
-        m2 = v;
-      }
-    }
-    s_gs[lane] = m1 + m2;
-  }
-  __syncthreads();
-  if (lane < n_group) {
-    const float mine = s_gs[lane];
-    int rank = 0;
-    for (int o = 0; o < n_group; ++o) {
-      const float v = s_gs[o];
-      rank += (v > mine) || (v == mine && o < lane);
-    }
-    s_keep[lane] = rank < topk_group;
-  }
-  __syncthreads();
-
-  // each lane holds experts lane + 64*m, masked to -inf outside kept groups
-  float v[kMaxE / 64];
+  // group scores
+  const int lpg = E / (n_group * EPL);
+  float m1 = -INFINITY, m2 = -INFINITY;
 #pragma unroll
-  for (int m = 0; m < kMaxE / 64; ++m) {
-    const int e = lane + 64 * m;
-    v[m] = (e < E) ? (s_keep[e / gsize] ? s_sb[e] : -INFINITY) : -INFINITY;
+  for (int i = 0; i < EPL; ++i) {
+    const float v = valid[i] ? sb[i] : -INFINITY;
+    if (v > m1) {
+      m2 = m1;
+      m1 = v;
+    } else if (v > m2) {
+      m2 = v;
+    }
+  }
+  for (int off = 1; off < lpg; off <<= 1) {
+    const float o1 = __shfl_xor(m1, off), o2 = __shfl_xor(m2, off);
+    const float hi = fmaxf(m1, o1), lo1 = fminf(m1, o1), lo2 = fmaxf(m2, o2);
+    m1 = hi;
+    m2 = fmaxf(lo1, lo2);
+  }
+  const float gs = m1 + m2;
+  const int my_g = lane / lpg;
+  int rank = 0;
+  for (int o = 0; o < n_group; ++o) {
+    const float go = readlane_f32(gs, o * lpg);
+    rank += (go > gs) || (go == gs && o < my_g);
+  }
+  const bool keep = (lane * EPL < E) && rank < topk_group;
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    key[i] = valid[i] ? (((uint64_t)orderable(keep ? sb[i] : -INFINITY) << 32) |
+                         (uint64_t)(0xffffffffu - (uint32_t)e))
+                      : 0ull;
   }
   uint32_t taken = 0;
   float S = 0.0f;
+  int my_e = 0;
+  float my_s = 0.0f;
   for (int j = 0; j < K; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-    int have = 0;
+    uint64_t best = 0;
 #pragma unroll
-    for (int m = 0; m < kMaxE / 64; ++m) {
-      const int e = lane + 64 * m;
-      if (e < E && !((taken >> m) & 1u) && (!have || v[m] > bv)) {
-        bv = v[m];
-        be = e;
-        have = 1;
-      }
-    }
+    for (int i = 0; i < EPL; ++i)
+      if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
+    const uint64_t m = wave_max_u64(best);
+    const int e = (int)(0xffffffffu - (uint32_t)m);
+    const int owner = e / EPL, slot = e % EPL;
+    float sv = s[0];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      const int oh = __shfl_xor(have, off);
-      const bool better = oh && (!have || ov > bv || (ov == bv && oe < be));
-      if (better) {
-        bv = ov;
-        be = oe;
-        have = oh;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == 0) {
-      s_sel[j] = be;
-      S = (j == 0) ? s_s[be] : S + s_s[be];
+    for (int i = 1; i < EPL; ++i)
+      if (slot == i) sv = s[i];
+    const float ss = readlane_f32(sv, owner);
+    if (lane == owner) taken |= 1u << slot;
+    S = (j == 0) ? ss : S + ss;
+    if (lane == j) {
+      my_e = e;
+      my_s = ss;
     }
   }
-  if (lane == 0) {
+  if (lane < K) {
     const float d = S + 1e-20f;
-    for (int j = 0; j < K; ++j) {
-      const int e = s_sel[j];
-      const float qv = s_s[e] / d;
-      idx[(size_t)t * K + j] = e;
-      wout[(size_t)t * K + j] = qv * scale;
-    }
+    const float qv = my_s / d;
+    idx[(size_t)t * K + lane] = my_e;
+    wout[(size_t)t * K + lane] = qv * scale;
   }
 }
 
-hipError_t launch_select(const float* logits, const float* bias, int32_t* idx, float* w,
-                         uint32_t* status, int T, int E, int n_group, int topk_group, int K,
-                         float scale, bool record_nonfinite, hipStream_t s,
+int select_epl(int E) {
+  const int need = (E + 63) / 64;
+  int epl = 1;
+  while (epl < need) epl *= 2;
+  return epl;
+}
+
+hipError_t launch_select(const float* part, int ks, float* logits_out, const float* bias,
+                         int32_t* idx, float* w, uint32_t* status, int T, int E, int n_group,
+                         int topk_group, int K, float scale, bool record_nonfinite, hipStream_t s,
                          const StageTimer* tm) {
+  const dim3 grid((unsigned)((T + 3) / 4));
+  const int rec = record_nonfinite ? 1 : 0;
   stage_begin(tm, kSelect, s);
-  hipLaunchKernelGGL(k_select, dim3((unsigned)T), dim3(64), 0, s, logits, bias, idx, w, status, E,
-                     n_group, topk_group, K, scale, record_nonfinite ? 1 : 0);
+  switch (select_epl(E)) {
+    case 1:
+      hipLaunchKernelGGL(k_select<1>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
+                         status, T, E, n_group, topk_group, K, scale, rec);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_select<2>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
+                         status, T, E, n_group, topk_group, K, scale, rec);
+      break;
+    case 4:
+      hipLaunchKernelGGL(k_select<4>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
+                         status, T, E, n_group, topk_group, K, scale, rec);
+      break;
+    default:
+      hipLaunchKernelGGL(k_select<8>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
+                         status, T, E, n_group, topk_group, K, scale, rec);
+      break;
+  }
   stage_end(tm, kSelect, s);
   return hipGetLastError();
 }

@@ -140,31 +140,44 @@ def test_route_exact_other_shapes(shape):
 
 
 def test_route_nonfinite_flag():
+    """A NaN or Inf in x makes that token's logits non-finite (and only that
+    token's): the status bit is raised, its indices stay in range, every other
+    token is routed as usual."""
     say("route non-finite")
     Lb = L()
     rng = np.random.default_rng(7)
-    lam = rng.normal(0, 1, (6, 256)).astype(np.float32)
-    lam[2, 17] = np.nan
-    lam[4, 3] = np.inf
     T, E, H = 6, 256, 256
+    lam = rng.normal(0, 1, (T, E)).astype(np.float32)
     x = torch.zeros(T, H)
     x[torch.arange(T), torch.arange(T)] = 1.0
+    x[2, 100] = float("nan")
+    x[4, 101] = float("inf")
     wr = torch.zeros(E, H)
     wr[:, :T] = torch.from_numpy(lam.T.copy())
+    wr[:, 100:102] = 1.0  # inf * 1 stays infinite; other tokens multiply these by 0
     d = Lb.make_desc(T, H, I=64, I_shared=0, flags=Lb.MOE_F_CHECK_FINITE)
     idx = torch.empty(T, 8, dtype=torch.int32, device=DEV)
     w = torch.empty(T, 8, dtype=torch.float32, device=DEV)
+    lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
     ws = Lb.alloc_workspace(d, DEV)
-    Lb.moe_route(d, x.to(torch.bfloat16).to(DEV), wr.to(DEV), None, None, idx, w, ws)
+    Lb.moe_route(d, x.to(torch.bfloat16).to(DEV), wr.to(DEV), None, lg, idx, w, ws)
     st = Lb.moe_status(ws)
     assert st & Lb.MOE_STATUS_NONFINITE
     assert Lb.moe_status(ws) == 0  # cleared by the read
+    gl = lg.cpu().numpy()
+    assert not np.isfinite(gl[2]).any() and not np.isfinite(gl[4]).any()
+    ok = np.array([1, 1, 0, 1, 0, 1], bool)
+    np.testing.assert_array_equal(gl[ok], lam[ok])
     gi = idx.cpu().numpy()
     assert gi.min() >= 0 and gi.max() < E
-    ri, rw, rf = oracle.select(lam, None, 8, 4, 8, 2.5)
+    assert gi[2].tolist() == list(range(8)) and (w.cpu().numpy()[[2, 4]] == 0).all()
+    lam_nf = lam.copy()
+    lam_nf[2, :] = np.nan
+    lam_nf[4, :] = np.inf
+    ri, rw, rf = oracle.select(lam_nf, None, 8, 4, 8, 2.5)
     assert rf.tolist() == [0, 0, 1, 0, 1, 0]
-    ok = rf == 0
     np.testing.assert_array_equal(gi[ok], ri[ok])
+    np.testing.assert_array_equal(w.cpu().numpy()[ok].view(np.uint32), rw[ok].view(np.uint32))
 
 
 # --------------------------------------------------------------------------- routing, random inputs
