@@ -289,3 +289,26 @@ def moe_sigmoid32(z, s, stream=None):
     zp = _check(z, "z", tuple(z.shape), torch.float32, dev)
     sp = _check(s, "s", tuple(z.shape), torch.float32, dev)
     _rc(LIB.moe_sigmoid32(zp, sp, z.numel(), _stream(stream)), "moe_sigmoid32")
+
+
+def moe_stack_forward(d: MoeDesc, x, layers, ws, eps: float = 1e-6, tracking=None,
+                      idx_out=None, counts_out=None, on_layer=None, stream=None):
+    """A residual stack of MoE layers, each x <- RN(x + layer(RN(RMSNorm(x)))).
+
+    `x` [T][H] is updated in place; `layers` is a list of weight dicts;
+    tracking (optional, [L][E] int64) accumulates per-layer counts; idx_out /
+    counts_out (optional, [L][T][k] int32 / [L][E] int32) receive each
+    layer's routing.  on_layer(l, x) is called after layer l (for inspection).
+    Every step runs in libmoe kernels (moe_residual_rmsnorm, moe_layer_forward)."""
+    r = torch.empty_like(x)
+    y = torch.empty_like(x)
+    moe_residual_rmsnorm(d, x, None, x, r, eps, stream)
+    for l, w in enumerate(layers):
+        moe_layer_forward(d, r, w, y,
+                          topk_idx_out=None if idx_out is None else idx_out[l],
+                          counts_out=None if counts_out is None else counts_out[l],
+                          tracking=None if tracking is None else tracking[l], ws=ws, stream=stream)
+        moe_residual_rmsnorm(d, x, y, x, r, eps, stream)
+        if on_layer is not None:
+            on_layer(l, x)
+    return x

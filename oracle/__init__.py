@@ -63,8 +63,8 @@ def _load():
     lib.orc_logits.argtypes = [i32, i32, i32, P, i32, P, P, i32]
     lib.orc_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_float, P, P, P, P, P]
     lib.orc_select.restype = i32
-    lib.orc_route_intervals.argtypes = [i32, i32, i32, i32, i32, P, ctypes.c_double, P, P, P,
-                                        P, P, P, P]
+    lib.orc_route_intervals.argtypes = [i32, i32, i32, i32, i32, P, ctypes.c_double,
+                                        ctypes.c_double, P, P, P, P, P, P, P]
     lib.orc_route_intervals.restype = i32
     lib.orc_permute.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.orc_experts_path_a.argtypes = [P, P, i32, P, P, P, i32, P, i32]
@@ -158,8 +158,9 @@ def route(x, w_router, bias, n_group, topk_group, top_k, scale, nthreads=None):
 
 
 def route_intervals(l64: np.ndarray, tau: float, bias, n_group, topk_group, top_k,
-                    idx_ref: np.ndarray, want_bounds: bool = False):
-    """Decidedness of each token's selection under a +-tau band on every logit."""
+                    idx_ref: np.ndarray, want_bounds: bool = False, tau_rel: float = 0.0):
+    """Decidedness of each token's selection when every fp32 logit may lie
+    anywhere within tau + tau_rel*|l| of the fp64 logit l."""
     l64 = np.ascontiguousarray(l64, dtype=np.float64)
     T, E = l64.shape
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
@@ -171,7 +172,8 @@ def route_intervals(l64: np.ndarray, tau: float, bias, n_group, topk_group, top_
                       gs_lo=np.empty((T, n_group), np.float32),
                       gs_hi=np.empty((T, n_group), np.float32))
     g = (lambda k: _ptr(bounds[k]) if bounds else None)
-    rc = _load().orc_route_intervals(T, E, n_group, topk_group, top_k, _ptr(l64), tau, _ptr(b),
+    rc = _load().orc_route_intervals(T, E, n_group, topk_group, top_k, _ptr(l64), tau, tau_rel,
+                                     _ptr(b),
                                      _ptr(ref), _ptr(dec), g("sb_lo"), g("sb_hi"), g("gs_lo"),
                                      g("gs_hi"))
     if rc < 0:

@@ -382,14 +382,16 @@ int orc_select(int T, int E, int n_group, int topk_group, int K, float scale,
 /* ------------------------------------------------------------------------ */
 /* interval analysis (test helper)                                          */
 /* ------------------------------------------------------------------------ */
-/* If every fp32 logit lies in [l - tau, l + tau], then, sigma32 and fp32
+/* If every fp32 logit lies in [l - tau, l + tau], tau = tau_abs + tau_rel*|l|
+ * (the error of an fp32 dot product grows with the size of its partial sums),
+ * then, sigma32 and fp32
  * addition being monotone, every biased score lies in [sb_lo, sb_hi] and every
  * group score (a sum of the two largest) in [gs_lo, gs_hi].  The reference
  * selection idx_ref (made from RN32(l)) is the only possible one when the kept
  * groups and the chosen experts are separated from the rest by those bounds. */
 
 int orc_route_intervals(int T, int E, int n_group, int topk_group, int K,
-                        const double* logits, double tau, const float* bias,
+                        const double* logits, double tau_abs, double tau_rel, const float* bias,
                         const int32_t* idx_ref, uint8_t* decided, float* sb_lo_out,
                         float* sb_hi_out, float* gs_lo_out, float* gs_hi_out) {
   if (!select_valid(E, n_group, topk_group, K)) return -1;
@@ -407,6 +409,7 @@ int orc_route_intervals(int T, int E, int n_group, int topk_group, int K,
     const double* l = logits + (size_t)t * E;
     const int32_t* ref = idx_ref + (size_t)t * K;
     for (int e = 0; e < E; ++e) {
+      const double tau = tau_abs + tau_rel * fabs(l[e]);
       float a = nextafterf((float)(l[e] - tau), -INFINITY);
       float b = nextafterf((float)(l[e] + tau), INFINITY);
       float bb = bias ? bias[e] : 0.0f;

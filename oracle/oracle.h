@@ -52,12 +52,13 @@ int orc_select(int T, int E, int n_group, int topk_group, int K, float scale,
                const float* lam, const float* bias, int32_t* idx, float* w, uint8_t* flag);
 
 /* Interval analysis used to decide which tokens have a unique selection when
- * every fp32 logit may sit anywhere in [l - tau, l + tau] (l = fp64 logit).
+ * every fp32 logit may sit anywhere in [l - tau, l + tau] (l = fp64 logit,
+ * tau = tau_abs + tau_rel * |l|).
  * Writes per token: decided[t] bit0 = set of K experts unique, bit1 = also
  * their order unique; and the bounds sb_lo/sb_hi [T][E], gs_lo/gs_hi
  * [T][n_group] (fp32).  Any output pointer except decided may be NULL. */
 int orc_route_intervals(int T, int E, int n_group, int topk_group, int K,
-                        const double* logits, double tau, const float* bias,
+                        const double* logits, double tau_abs, double tau_rel, const float* bias,
                         const int32_t* idx_ref, uint8_t* decided, float* sb_lo,
                         float* sb_hi, float* gs_lo, float* gs_hi);
 
