@@ -110,6 +110,10 @@ int check_ws(const moe_desc_t& d, void* ws, size_t ws_bytes) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+int tile_rows(const moe_desc_t& d) {
+  return moe::expert_tile_rows(d.T, d.top_k, d.E, d.I, d.I_shared, d.dtype == MOE_BF16);
+}
+
 // route into (idx, w); logits_user (nullable) receives the fp32 logits
 int run_route(const moe_desc_t& d, const void* x, const float* w_router, const float* bias,
               float* logits_user, int32_t* idx, float* w, void* ws, hipStream_t s,
@@ -147,7 +151,7 @@ int run_permute(const moe_desc_t& d, const int32_t* idx, int32_t* counts, int32_
                 hipStream_t s, const moe::StageTimer* tm = nullptr) {
   const Layout L = make_layout(d);
   return hip_rc(moe::launch_permute(idx, (int64_t)d.T * d.top_k, d.E, d.T, d.I_shared,
-                                    at<int32_t>(ws, L.perm), counts, offsets, sorted_pair,
+                                    tile_rows(d), at<int32_t>(ws, L.perm), counts, offsets, sorted_pair,
                                     pair_slot, tracking, at<int32_t>(ws, L.tile_off),
                                     at<uint32_t>(ws, L.status), s, tm));
 }
@@ -178,6 +182,7 @@ int run_experts(const moe_desc_t& d, const void* x, const float* topk_w, const i
   a.y = y;
   a.tile_off = at<int32_t>(ws, L.tile_off);
   a.tiles_ready = tiles_ready;
+  a.tile_rows = tile_rows(d);
   a.h_routed = at<void>(ws, L.h_routed);
   a.h_shared = at<void>(ws, L.h_shared);
   a.o_routed = at<void>(ws, L.o_routed);

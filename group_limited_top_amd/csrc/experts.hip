@@ -22,26 +22,36 @@
 //            bf16 block in registers, giving 8 MFMA tiles whose row m maps to
 //            h = h0 + 8m + j.
 #include "device.h"
+#include "expert_tiles.h"
 #include "kernels.h"
 
 namespace moe {
 
-int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is) {
+int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows) {
   const int64_t P = T * K;
-  int64_t n = (P + kTileRows - 1) / kTileRows + E;
-  if (Is > 0) n += (T + kTileRows - 1) / kTileRows;
+  int64_t n = (P + tile_rows - 1) / tile_rows + E;
+  if (Is > 0) n += (T + tile_rows - 1) / tile_rows;
   return n;
+}
+
+// Few rows per expert (on average fewer than kTiledRows / 2): stream each
+// expert's weights once past its rows; otherwise tile the GEMMs in LDS (bf16,
+// feature sizes in whole 128-wide slices).
+int expert_tile_rows(int64_t T, int K, int E, int I, int Is, bool bf16) {
+  const bool tiled_ok = bf16 && I % 128 == 0 && Is % 128 == 0;
+  return (tiled_ok && (T * K) / E >= kTiledRows / 2) ? kTiledRows : kTileRows;
 }
 
 // tile_off[g] = number of tiles of "experts" 0..g-1 (E + 1 of them, the last
 // is the shared expert with T rows when Is > 0); tile_off[E + 1] = total.
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offsets, int E, int T,
-                                                 int Is, int32_t* __restrict__ tile_off) {
+                                                 int Is, int tile_rows,
+                                                 int32_t* __restrict__ tile_off) {
   __shared__ int32_t sc[1024];
   const int g = threadIdx.x;
   int32_t n = 0;
-  if (g < E) n = (offsets[g + 1] - offsets[g] + kTileRows - 1) / kTileRows;
-  else if (g == E && Is > 0) n = (T + kTileRows - 1) / kTileRows;
+  if (g < E) n = (offsets[g + 1] - offsets[g] + tile_rows - 1) / tile_rows;
+  else if (g == E && Is > 0) n = (T + tile_rows - 1) / tile_rows;
   sc[g] = n;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
@@ -54,28 +64,10 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offs
   if (g == E) tile_off[E + 1] = sc[g];
 }
 
-struct TileInfo {
-  int e;       // expert, E = shared
-  bool shared;
-  int row0;    // first row (sorted pair row, or token for the shared expert)
-  int nrows;   // rows in this tile, 1..kTileRows
-};
-
-// Returns false when `tile` is past the last tile.
-__device__ __forceinline__ bool decode_tile(const ExpertArgs& a, int tile, TileInfo& ti) {
-  if (tile >= a.tile_off[a.E + 1]) return false;
-  const int e = upper_bound_i32(a.tile_off, a.E + 2, tile) - 1;
-  const int m = tile - a.tile_off[e];
-  ti.e = e;
-  ti.shared = (e == a.E);
-  if (ti.shared) {
-    ti.row0 = m * kTileRows;
-    ti.nrows = min(kTileRows, a.T - ti.row0);
-  } else {
-    ti.row0 = a.offsets[e] + m * kTileRows;
-    ti.nrows = min(kTileRows, a.offsets[e + 1] - ti.row0);
-  }
-  return true;
+hipError_t launch_tiles(const ExpertArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_rows,
+                     a.tile_off);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
@@ -330,6 +322,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
 }
 
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
+  if (a.tile_rows == kTiledRows) return launch_experts_tiled_bf16(a, s, tm);
   // the down kernel's LDS tile can exceed the 64 KiB default for I > 960
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k_down_bf16), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -337,10 +330,10 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
   if (attr != hipSuccess) return attr;
   if (!a.tiles_ready) {
     stage_begin(tm, kTiles, s);
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
+    (void)launch_tiles(a, s);
     stage_end(tm, kTiles, s);
   }
-  const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is);
+  const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
   const int imax = a.I > a.Is ? a.I : a.Is;
   const int slices = imax / 64;
   stage_begin(tm, kGateUp, s);
@@ -351,6 +344,12 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
   stage_begin(tm, kDown, s);
   hipLaunchKernelGGL(k_down_bf16, dim3((unsigned)(tiles * hslices)), dim3(256), lds, s, a, hslices);
   stage_end(tm, kDown, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_combine_bf16(a, s, tm);
+}
+
+hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
   stage_begin(tm, kCombine, s);
   hipLaunchKernelGGL(k_combine_bf16, dim3((unsigned)a.T), dim3(256), 0, s, a);
   stage_end(tm, kCombine, s);
@@ -479,10 +478,10 @@ __global__ __launch_bounds__(256) void k_combine_f32(const ExpertArgs a) {
 hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
   if (!a.tiles_ready) {
     stage_begin(tm, kTiles, s);
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_off);
+    (void)launch_tiles(a, s);
     stage_end(tm, kTiles, s);
   }
-  const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is);
+  const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
   const int imax = a.I > a.Is ? a.I : a.Is;
   const int slices = imax / 64;
   stage_begin(tm, kGateUp, s);

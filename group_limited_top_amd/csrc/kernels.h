@@ -7,7 +7,10 @@
 
 namespace moe {
 
-constexpr int kTileRows = 32;  // token rows per expert tile
+constexpr int kTileRows = 32;    // token rows per tile of the weight-streaming kernels
+constexpr int kTiledRows = 128;  // token rows per tile of the LDS-tiled kernels
+// Rows per expert tile for a layer: many rows per expert -> LDS-tiled GEMMs.
+int expert_tile_rows(int64_t T, int K, int E, int I, int Is, bool bf16);
 
 // Optional event pair around one kernel stage (see moe_layer_forward_timed).
 struct StageTimer {
@@ -43,10 +46,11 @@ hipError_t launch_sigmoid32(const float* z, float* out, int64_t n, hipStream_t s
 
 // Permute ---------------------------------------------------------------------
 size_t permute_scratch_ints(int64_t P, int E);
-hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int32_t* scratch,
-                          int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                          int32_t* pair_slot, int64_t* tracking, int32_t* tile_off,
-                          uint32_t* status, hipStream_t s, const StageTimer* tm = nullptr);
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int tile_rows,
+                          int32_t* scratch, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking,
+                          int32_t* tile_off, uint32_t* status, hipStream_t s,
+                          const StageTimer* tm = nullptr);
 
 // Experts ---------------------------------------------------------------------
 
@@ -62,13 +66,16 @@ struct ExpertArgs {
   void* y;
   // workspace
   int32_t* tile_off;  // [E+2]
+  int tile_rows;      // token rows per tile (kTileRows or kTiledRows)
   bool tiles_ready;   // tile_off already built (by the permute kernels)
   void* h_routed;     // [P][I]
   void* h_shared;     // [T][Is]
   void* o_routed;     // [P][H]
   void* o_shared;     // [T][H]
 };
-int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is);
+int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows);
+hipError_t launch_experts_tiled_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
+hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm = nullptr);
 hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTimer* tm = nullptr);
 

@@ -10,7 +10,7 @@
 // its group; per-wave running counts live in LDS.  Everything is integer
 // arithmetic in a fixed order, so results are deterministic.
 //
-// The same kernels also build the expert-tile list (tile_off, kTileRows rows
+// The same kernels also build the expert-tile list (tile_off, tile_rows rows
 // per tile; the shared expert is "expert" E with T rows) used by the expert
 // kernels.
 //
@@ -61,7 +61,8 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* sc) {
 }
 
 // counts/offsets/tracking/tile_off from per-expert totals held by thread e.
-__device__ __forceinline__ void finish_counts(int32_t total, int E, int T, int Is, int32_t* sc,
+__device__ __forceinline__ void finish_counts(int32_t total, int E, int T, int Is, int tile_rows,
+                                              int32_t* sc,
                                               int32_t* counts, int32_t* offsets,
                                               int32_t* offs_lds, int64_t* tracking,
                                               int32_t* tile_off) {
@@ -74,10 +75,10 @@ __device__ __forceinline__ void finish_counts(int32_t total, int E, int T, int I
     if (tracking) tracking[e] += (int64_t)total;
   }
   if (e == E - 1) offsets[E] = incl;
-  // tiles of kTileRows rows per expert, the shared expert last
+  // tiles of tile_rows rows per expert, the shared expert last
   int32_t n = 0;
-  if (e < E) n = (total + kTileRows - 1) / kTileRows;
-  else if (e == E && Is > 0) n = (T + kTileRows - 1) / kTileRows;
+  if (e < E) n = (total + tile_rows - 1) / tile_rows;
+  else if (e == E && Is > 0) n = (T + tile_rows - 1) / tile_rows;
   const int32_t tin = block_scan_1024(n, sc);
   if (e <= E) tile_off[e] = tin - n;
   if (e == E) tile_off[E + 1] = tin;
@@ -90,7 +91,8 @@ constexpr int kSmallWaves = 16, kSmallBatches = 16;
 constexpr int kSmallMaxP = kSmallWaves * kSmallBatches * 64;
 
 __global__ __launch_bounds__(1024) void k_permute_small(
-    const int32_t* __restrict__ idx, int P, int E, int T, int Is, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int P, int E, int T, int Is, int tile_rows,
+    int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_slot, int64_t* __restrict__ tracking,
     int32_t* __restrict__ tile_off, uint32_t* __restrict__ status) {
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(1024) void k_permute_small(
       total += c;
     }
   }
-  finish_counts(total, E, T, Is, sc, counts, offsets, offs, tracking, tile_off);
+  finish_counts(total, E, T, Is, tile_rows, sc, counts, offsets, offs, tracking, tile_off);
   __syncthreads();
 #pragma unroll
   for (int b = 0; b < kSmallBatches; ++b) {
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(256) void k_perm_rank(const int32_t* __restrict__ i
 
 __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ chunk_hist,
                                                      int nchunks, int E, int T, int Is,
+                                                     int tile_rows,
                                                      int32_t* __restrict__ chunk_base,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
       }
     }
   }
-  finish_counts(total, E, T, Is, sc, counts, offsets, nullptr, tracking, tile_off);
+  finish_counts(total, E, T, Is, tile_rows, sc, counts, offsets, nullptr, tracking, tile_off);
 }
 
 __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ idx, int64_t P,
@@ -263,14 +266,16 @@ size_t permute_scratch_ints(int64_t P, int E) {
   return (size_t)P + 2 * (size_t)nch * E;  // prank, chunk_hist, chunk_base
 }
 
-hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int32_t* scratch,
-                          int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                          int32_t* pair_slot, int64_t* tracking, int32_t* tile_off,
-                          uint32_t* status, hipStream_t s, const StageTimer* tm) {
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int tile_rows,
+                          int32_t* scratch, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking,
+                          int32_t* tile_off, uint32_t* status, hipStream_t s,
+                          const StageTimer* tm) {
   if (P <= kSmallMaxP) {
     stage_begin(tm, kHist, s);
-    hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, s, idx, (int)P, E, T, Is, counts,
-                       offsets, sorted_pair, pair_slot, tracking, tile_off, status);
+    hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, s, idx, (int)P, E, T, Is,
+                       tile_rows, counts, offsets, sorted_pair, pair_slot, tracking, tile_off,
+                       status);
     stage_end(tm, kHist, s);
     return hipGetLastError();
   }
@@ -284,8 +289,8 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, i
                      chunk_hist, status);
   stage_end(tm, kHist, s);
   stage_begin(tm, kScan, s);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E, T, Is, chunk_base,
-                     counts, offsets, tracking, tile_off);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E, T, Is, tile_rows,
+                     chunk_base, counts, offsets, tracking, tile_off);
   stage_end(tm, kScan, s);
   stage_begin(tm, kScatter, s);
   hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, idx, P, E,

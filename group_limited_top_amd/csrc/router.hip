@@ -109,7 +109,12 @@ hipError_t launch_split_router(const float* w, uint16_t* split, int E, int H, hi
 // most a few blocks) or copied from the pre-split planes (large T).  x rows go
 // straight from global memory into the A operands.
 // ----------------------------------------------------------------------------
-constexpr int kLgBM = 64, kLgBN = 64, kLgKC = 64, kLgRow = kLgKC + 8;  // +8: bank spread
+constexpr int kLgBM = 64, kLgBN = 64, kLgKC = 64, kLgRow = kLgKC;
+
+// LDS element offset of 16-byte chunk c (8 bf16) of staged weight row r: the
+// chunk index is XORed with bits 1..3 of the row, so that 16 consecutive rows
+// at one chunk (or two chunks) land on disjoint banks with 64 or 128 banks.
+__device__ __forceinline__ int lg_swz(int r, int c) { return r * kLgRow + ((c ^ ((r >> 1) & 7)) << 3); }
 constexpr int kMaxKSplit = 16;
 
 __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
@@ -172,8 +177,8 @@ __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict_
     }
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
-      st16(&wl[buf][p][er][ks16], o[2 * p]);
-      st16(&wl[buf][p][er][ks16 + 8], o[2 * p + 1]);
+      st16(&wl[buf][p][0][0] + lg_swz(er, ks16 / 8), o[2 * p]);
+      st16(&wl[buf][p][0][0] + lg_swz(er, ks16 / 8 + 1), o[2 * p + 1]);
     }
   };
 
@@ -201,7 +206,8 @@ __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict_
       for (int n = 0; n < 4; ++n) {
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(&wl[buf][p][n * 16 + r][s * 32 + q * 8]);
+          const u32x4 b =
+              *reinterpret_cast<const u32x4*>(&wl[buf][p][0][0] + lg_swz(n * 16 + r, s * 4 + q));
           acc[n] = mfma16x16x32(a_cur[s], b, acc[n]);
         }
       }
