@@ -111,7 +111,7 @@ int check_ws(const moe_desc_t& d, void* ws, size_t ws_bytes) {
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 int tile_rows(const moe_desc_t& d) {
-  return moe::expert_tile_rows(d.T, d.top_k, d.E, d.I, d.I_shared, d.dtype == MOE_BF16);
+  return moe::expert_tile_rows(d.T, d.top_k, d.E, d.I, d.I_shared, d.H, d.dtype == MOE_BF16);
 }
 
 // route into (idx, w); logits_user (nullable) receives the fp32 logits

@@ -35,10 +35,13 @@ int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows) {
 }
 
 // Few rows per expert (on average fewer than kTiledRows / 2): stream each
-// expert's weights once past its rows; otherwise tile the GEMMs in LDS (bf16,
-// feature sizes in whole 128-wide slices).
-int expert_tile_rows(int64_t T, int K, int E, int I, int Is, bool bf16) {
-  const bool tiled_ok = bf16 && I % 128 == 0 && Is % 128 == 0;
+// expert's weights once past its rows; otherwise run the LDS-pipelined GEMMs
+// (bf16, feature sizes in whole 128-wide slices, token and hidden arrays
+// addressable with 32-bit byte offsets).
+int expert_tile_rows(int64_t T, int K, int E, int I, int Is, int H, bool bf16) {
+  const int64_t imax = I > Is ? I : Is;
+  const bool tiled_ok = bf16 && I % 128 == 0 && Is % 128 == 0 && H % 128 == 0 &&
+                        T * H * 2 < (int64_t(1) << 32) && T * K * imax * 2 < (int64_t(1) << 32);
   return (tiled_ok && (T * K) / E >= kTiledRows / 2) ? kTiledRows : kTileRows;
 }
 

@@ -1,21 +1,26 @@
-// experts_tiled.hip -- LDS-tiled MFMA grouped GEMMs for experts with many
-// rows (a large batch of tokens).
+// experts_tiled.hip -- MFMA grouped GEMMs for experts with many rows (a large
+// batch of tokens).
 //
 // [Routing §四]: every expert is down(silu(gate x) * up x) over stacked
 // [E][I][H] weights; [Routing §五]: the shared expert is one more bucket (all T
 // tokens).  Rows are the expert-sorted pairs; a tile is kTiledRows rows of one
-// expert.  Both kernels stage 32-deep K slices of both operands in LDS (two
-// stages, one barrier per stage) and run 16x16x32 bf16 MFMAs with the weights
+// expert.
+//
+// Data flow.  A block is 8 waves (two per SIMD) over one 128-row token tile.
+// Each weight element is used by exactly one wave, so weights go from global
+// memory straight into registers in MFMA operand layout (no LDS round trip);
+// the token tile, which all 8 waves use, is staged in LDS in 64-deep K slices
+// (two stages, one barrier per stage).  16x16x32 bf16 MFMAs take the weights
 // as the A operand and the token rows as B, so that each lane ends holding
 // consecutive output features of one token (wide stores).
 //
-//   gate/up: block = 128 tokens x 128 features (256 weight rows: 128 gate +
-//            128 up); wave (wi, wt) = 64 features of both gate and up x 64
-//            tokens (8 x 4 MFMA tiles); epilogue h = silu(g) * u in registers.
-//   down:    block = 256 output columns x 128 tokens; W_down[e] is [I][H] (H
-//            contiguous), staged as [i][h] rows; each lane reads 8 consecutive
-//            h at 8 consecutive i and transposes the 8x8 block in registers,
-//            giving 8 MFMA tiles whose row m maps to h = h0 + 8m + j.
+//   gate/up: block = 128 tokens x 256 features; wave w = 32 features of both
+//            gate and up x 128 tokens (2 x 2 x 8 MFMA tiles); epilogue
+//            h = silu(g) * u in registers.
+//   down:    block = 128 tokens x 512 output columns; wave w = 64 columns.
+//            W_down[e] is [I][H] (H contiguous): each lane loads 4
+//            consecutive h at 8 consecutive i and transposes the 8x4 block in
+//            registers, giving 4 MFMA tiles whose row m maps to h = h0 + 4m + j.
 //
 // Blocks are launched in a multiple of 8 and mapped so that each XCD (blocks
 // b with equal b mod 8) works on consecutive tiles, i.e. on the same experts,
@@ -26,18 +31,71 @@
 
 namespace moe {
 
-constexpr int kTBK = 32;                       // K depth of one LDS stage
-constexpr int kTRow = kTBK * 2;                // bytes per staged row (four 16-byte chunks)
-constexpr int kGuWRows = 256;                  // weight rows per gate/up block
-constexpr int kGuRows = kGuWRows + kTiledRows;  // staged rows per gate/up stage
-constexpr int kDnCols = 256;                   // output columns per down block
-constexpr int kDnWRow = kDnCols * 2 + 32;      // bytes per staged W_down row (+32: bank spread)
+// Pipeline.  Every stage is a 32-deep K slice of 640 rows x 64 bytes
+// (40 KiB): 512 weight rows (gate/up) or 32 W_down rows of 1 KiB (down), plus
+// the 128 token rows.  Four stages (160 KiB, all of the CU's LDS) form a ring
+// filled by direct global -> LDS loads (global_load_lds_dwordx4: each wave
+// instruction writes 1 KiB, lane l at +16 l), so three stages are in flight
+// while one is computed, without holding any of it in registers.  Each of the
+// 4 waves issues 10 such loads per stage; before computing stage c a wave
+// waits until at most the 20 loads of stages c+1, c+2 are outstanding, then
+// all waves meet at a barrier.
+constexpr int kTBK = 32;                 // K depth of one stage
+constexpr int kRowB = kTBK * 2;          // bytes per staged token / gate-up weight row
+constexpr int kStageB = 40960;           // bytes per stage
+constexpr int kTokOff = 32768;           // token rows start here in a stage
+constexpr int kDmaPerWave = 10;          // 1 KiB loads per wave per stage
+constexpr int kGuFeat = 256;             // features per gate/up block (64 per wave)
+constexpr int kDnCols = 512;             // output columns per down block (128 per wave)
 
-// LDS position of 16-byte chunk c of staged row r.  Rows are 64 bytes; the
-// chunk index is XORed with bits 2..3 of the row so that the 16 (or 32) lanes
-// one ds_read_b128 serves at a time -- 16 consecutive rows at one chunk, or
-// two chunks -- fall on disjoint banks with either 64 or 128 four-byte banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * kTRow + ((c ^ ((r >> 2) & 3)) << 4); }
+typedef __attribute__((address_space(3))) const void lvoid_t;
+
+// One stage's 10 loads of this wave: load g (0..9) brings the lane's 16 bytes
+// from base[g] + off[g] (a wave-uniform 64-bit base plus a 32-bit per-lane
+// byte offset) into LDS lds + 4096 g + 16 * lane (global_load_lds_dwordx4,
+// M0 = the wave's LDS destination).  Written as inline asm so that the
+// compiler does not treat the ring's later LDS reads as dependent on every
+// load in flight; the ring orders them itself (ring_sync).  The memory clobber
+// keeps LDS reads from moving across it.
+__device__ __forceinline__ void dma_stage(const void* const (&base)[kDmaPerWave],
+                                          const uint32_t (&off)[kDmaPerWave], uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %20\n\t"
+      "global_load_lds_dwordx4 %0, %10\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %1, %11\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %2, %12\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %3, %13\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %4, %14\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %5, %15\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %6, %16\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %7, %17\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %8, %18\n\ts_add_u32 m0, m0, 4096\n\t"
+      "global_load_lds_dwordx4 %9, %19" ::"v"(off[0]),
+      "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]), "v"(off[7]),
+      "v"(off[8]), "v"(off[9]), "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3]),
+      "s"(base[4]), "s"(base[5]), "s"(base[6]), "s"(base[7]), "s"(base[8]), "s"(base[9]),
+      "s"(lds)
+      : "memory", "m0", "scc");
+}
+
+// LDS byte address of wave w's first 1 KiB slot in a stage buffer.
+__device__ __forceinline__ uint32_t wave_slot(const uint8_t* stage, int wave) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lvoid_t*)stage)) + 1024u * wave);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all its LDS operations are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void ring_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Swizzled position of 16-byte chunk c of a 64-byte staged row r: the chunk
+// index is XORed with bits 2..3 of the row, so that 16 consecutive rows read
+// at one chunk index fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ ((r >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ int xcd_logical(int b, int n) {  // n: a multiple of 8
   return (b & 7) * (n >> 3) + (b >> 3);
@@ -47,105 +105,142 @@ __device__ __forceinline__ u32x4 lds16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_gateup_tiled(const ExpertArgs a, int nslices,
-                                                          int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kGuRows * kTRow];
-  const int lb = xcd_logical(blockIdx.x, nblocks);
-  const int slice = lb % nslices;
-  TileInfo ti;
-  if (!decode_tile(a, lb / nslices, ti)) return;
-  const int I = ti.shared ? a.Is : a.I;
-  const int i0 = slice * 128;
-  if (i0 >= I) return;
-  const int H = a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
-  const int wi = wave & 1, wt = wave >> 1;
-
-  // staging role: row rr (+64 u), 16-byte column c16 of the 64-byte slice row
-  const int rr = tid >> 2, c16 = tid & 3;
-  const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
-  const uint16_t* wg = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_gate : a.w_gate) + ebase +
-                       (size_t)(i0 + rr) * H + c16 * 8;
-  const uint16_t* wu = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_up : a.w_up) + ebase +
-                       (size_t)(i0 + rr) * H + c16 * 8;
-  const uint16_t* xp[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = u * 64 + rr;
-    xp[u] = nullptr;
-    if (row < ti.nrows) {
-      const int tok = ti.shared ? ti.row0 + row : a.sorted_pair[ti.row0 + row] / a.K;
-      xp[u] = reinterpret_cast<const uint16_t*>(a.x) + (size_t)tok * H + c16 * 8;
-    }
+// The ring.  Stages are loaded in order (dma(buf) issues this wave's 10
+// loads of the next stage into buf).  A stage's operands are read from LDS
+// into one of two register sets (read(buf, set)) while the MFMAs of the
+// previous stage are still being issued: mfma(set, half) runs half of a
+// stage's MFMAs, and the barrier of stage c + 1 sits between the two halves
+// of stage c, so the LDS latency of stage c + 1 hides behind the second half.
+// Stage c + 4 goes into stage c's buffer once all waves have read stage c
+// (ring_sync waits for this wave's LDS reads before the barrier).
+// nk (stages) must be a positive multiple of 4.
+template <class Dma, class Read, class Mfma>
+__device__ __forceinline__ void run_ring(int nk, uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
+                                         Dma&& dma, Read&& read, Mfma&& mfma) {
+  constexpr int kTwo = 2 * kDmaPerWave;
+  dma(s0);
+  dma(s1);
+  dma(s2);
+  ring_sync<kTwo>();  // stage 0 landed (stages 1, 2 may be in flight)
+  dma(s3);
+  read(s0, 0);
+  // steady state: stages c .. c+3; stage c + k + 4 goes into stage c + k's buffer
+  for (int c = 0; c < nk - 4; c += 4) {
+    mfma(0, 0); ring_sync<kTwo>(); dma(s0); read(s1, 1); mfma(0, 1);
+    mfma(1, 0); ring_sync<kTwo>(); dma(s1); read(s2, 0); mfma(1, 1);
+    mfma(0, 0); ring_sync<kTwo>(); dma(s2); read(s3, 1); mfma(0, 1);
+    mfma(1, 0); ring_sync<kTwo>(); dma(s3); read(s0, 0); mfma(1, 1);
   }
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 sa[6], sb[6];  // global loads of two future stages in flight
-  auto gload = [&](u32x4 (&st)[6], int k0) {
-    st[0] = ld16(wg + k0);
-    st[1] = ld16(wg + (size_t)64 * H + k0);
-    st[2] = ld16(wu + k0);
-    st[3] = ld16(wu + (size_t)64 * H + k0);
-    st[4] = xp[0] ? ld16(xp[0] + k0) : zero4;
-    st[5] = xp[1] ? ld16(xp[1] + k0) : zero4;
-  };
-  auto sstore = [&](const u32x4 (&st)[6], int stage) {
-    uint8_t* base = lds[stage];
+  // last four stages: nothing more to load
+  mfma(0, 0); ring_sync<kTwo>(); read(s1, 1); mfma(0, 1);
+  mfma(1, 0); ring_sync<kDmaPerWave>(); read(s2, 0); mfma(1, 1);
+  mfma(0, 0); ring_sync<0>(); read(s3, 1); mfma(0, 1);
+  mfma(1, 0); mfma(1, 1);
+}
+
+// Source of this lane's token-row chunk in load j (8 or 9) of wave w: token
+// row 64 (j - 8) + 16 w + lane / 4, logical chunk (lane & 3) ^ ((lane >> 4) & 3).
+__device__ __forceinline__ int token_row_of(int j, int wave, int lane) {
+  return 64 * (j - 8) + 16 * wave + (lane >> 2);
+}
+__device__ __forceinline__ int chunk_of(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
+
+// ----------------------------------------------------------------------------
+// gate/up: block = 128 tokens x 256 features; wave w = 64 features (64 gate +
+// 64 up rows) x 128 tokens, 8 x 8 MFMA tiles.  Stage rows 0..255 are gate rows
+// i0.., 256..511 up rows, 512..639 tokens.  FULL: all 128 token rows present.
+template <bool FULL>
+__device__ __forceinline__ void gateup_tile(const ExpertArgs& a, const TileInfo& ti, int slice,
+                                            uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3) {
+  const int I = ti.shared ? a.Is : a.I;
+  const int i0 = slice * kGuFeat;
+  const int H = a.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int f0 = i0 + 64 * wave;
+  const bool wact = f0 < I;  // wave-uniform; idle waves still load and sync
+
+  // load g < 8: weight rows i0 + 64 (g & 3) + 16 w + lane / 4 of gate (g < 4) or
+  // up, clamped into range; loads 8, 9: token rows.  Byte offsets are fixed,
+  // the wave-uniform bases advance by one stage per dma().
+  const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
+  const int ck = chunk_of(lane);
+  const int wr = i0 + 16 * wave + (lane >> 2);
+  uint32_t off[kDmaPerWave];
 #pragma unroll
-    for (int u = 0; u < 6; ++u) st16(base + swz(64 * u + rr, c16), st[u]);
+  for (int j = 0; j < 4; ++j) {
+    off[j] = (uint32_t)(((size_t)min(wr + 64 * j, I - 1) * H + ck * 8) * 2);
+    off[4 + j] = off[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int row = token_row_of(8 + j, wave, lane);
+    if (row >= ti.nrows) row = 0;  // padding rows load row 0; their outputs are not stored
+    const int tok = ti.shared ? ti.row0 + row : a.sorted_pair[ti.row0 + row] / a.K;
+    off[8 + j] = (uint32_t)(((size_t)tok * H + ck * 8) * 2);
+  }
+  const uint16_t* gp = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_gate : a.w_gate) + ebase;
+  const uint16_t* up = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_up : a.w_up) + ebase;
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(a.x);
+  auto dma = [&](uint8_t* st) {
+    const void* base[kDmaPerWave] = {gp, gp, gp, gp, up, up, up, up, xp, xp};
+    dma_stage(base, off, wave_slot(st, wave));
+    gp += kTBK;
+    up += kTBK;
+    xp += kTBK;
   };
-  // tokens of this wave that exist (wave-uniform)
-  const int wrows = ti.nrows - wt * 64;
-  f32x4 acc[8][4];
+
+  f32x4 acc[8][8];  // [gate s = 0..3, up s = 4..7][token sub-tile n]
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[s][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 8; ++n) acc[s][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nsub = (ti.nrows + 15) >> 4;
 
-  auto compute = [&](int stage) {
-    const uint8_t* base = lds[stage];
-    u32x4 A[8], B[4];
+  u32x4 A[2][8], B[2][8];  // two operand sets: [set][gate s = 0..3, up s = 4..7], [set][n]
+  auto read = [&](const uint8_t* st, int set) {
+    if (!wact) return;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      A[s] = lds16(base + swz(wi * 64 + s * 16 + r16, q));
-      A[4 + s] = lds16(base + swz(128 + wi * 64 + s * 16 + r16, q));
+    for (int t = 0; t < 2; ++t) {
+      if (t != set) continue;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        A[t][u] = lds16(st + swz(64 * wave + 16 * u + r16, q));
+        A[t][4 + u] = lds16(st + swz(256 + 64 * wave + 16 * u + r16, q));
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        if (FULL || n < nsub) B[t][n] = lds16(st + swz(512 + 16 * n + r16, q));
     }
+  };
+  auto mfma = [&](int set, int half) {
+    if (!wact) return;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) B[n] = lds16(base + swz(256 + wt * 64 + n * 16 + r16, q));
+    for (int t = 0; t < 2; ++t) {
+      if (t != set) continue;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (n * 16 < wrows) {
+      for (int h = 0; h < 2; ++h) {
+        if (h != half) continue;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) acc[s][n] = mfma16x16x32(A[s], B[n], acc[s][n]);
+        for (int n = 4 * h; n < 4 * h + 4; ++n) {
+          if (FULL || n < nsub) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u][n] = mfma16x16x32(A[t][u], B[t][n], acc[u][n]);
+          }
+        }
       }
     }
   };
 
-  // stage c is computed from LDS buffer c & 1 while the global loads of
-  // stages c + 1 and c + 2 are in flight (register sets alternate)
-  const int nk = H / kTBK;
-  gload(sa, 0);
-  if (nk > 1) gload(sb, kTBK);
-  sstore(sa, 0);
-  __syncthreads();
-  for (int c = 0; c < nk; c += 2) {
-    if (c + 2 < nk) gload(sa, (c + 2) * kTBK);
-    compute(0);
-    if (c + 1 < nk) sstore(sb, 1);
-    __syncthreads();
-    if (c + 1 >= nk) break;
-    if (c + 3 < nk) gload(sb, (c + 3) * kTBK);
-    compute(1);
-    if (c + 2 < nk) sstore(sa, 0);
-    __syncthreads();
-  }
+  run_ring(H / kTBK, s0, s1, s2, s3, dma, read, mfma);
+  if (!wact) return;
 
-  // epilogue: lane holds features i0 + 64 wi + 16 s + 4q + 0..3 of token row 64 wt + 16 n + r16
+  // epilogue: lane holds features f0 + 16 s + 4q + 0..3 of token row 16 n + r16
   uint16_t* hbase = reinterpret_cast<uint16_t*>(ti.shared ? a.h_shared : a.h_routed);
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int row = wt * 64 + n * 16 + r16;
+  for (int n = 0; n < 8; ++n) {
+    const int row = 16 * n + r16;
     if (row < ti.nrows) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -155,14 +250,30 @@ __global__ __launch_bounds__(256, 2) void k_gateup_tiled(const ExpertArgs a, int
         u32x2 pk;
         pk.x = pack_bf16x2(hv[0], hv[1]);
         pk.y = pack_bf16x2(hv[2], hv[3]);
-        *reinterpret_cast<u32x2*>(hbase + (size_t)(ti.row0 + row) * I + i0 + wi * 64 + s * 16 +
-                                  4 * q) = pk;
+        *reinterpret_cast<u32x2*>(hbase + (size_t)(ti.row0 + row) * I + f0 + 16 * s + 4 * q) = pk;
       }
     }
   }
 }
 
+__global__ __launch_bounds__(256, 1) void k_gateup_tiled(const ExpertArgs a, int nslices,
+                                                          int nblocks) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s3[kStageB];
+  const int lb = xcd_logical(blockIdx.x, nblocks);
+  const int slice = lb % nslices;
+  TileInfo ti;
+  if (!decode_tile(a, lb / nslices, ti)) return;
+  if (slice * kGuFeat >= (ti.shared ? a.Is : a.I)) return;
+  if (ti.nrows == kTiledRows) gateup_tile<true>(a, ti, slice, s0, s1, s2, s3);
+  else gateup_tile<false>(a, ti, slice, s0, s1, s2, s3);
+}
+
 // ----------------------------------------------------------------------------
+// v[r] holds W[k = r][h = 0..7]; a[j] gets W[k = 0..7][h = j] as four k-pairs,
+// i.e. the A-operand row of column h = j.
 __device__ __forceinline__ void transpose8x8(const u32x4 (&v)[8], u32x4 (&a)[8]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -175,96 +286,97 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&v)[8], u32x4 (&a)[8])
   }
 }
 
-__global__ __launch_bounds__(256, 2) void k_down_tiled(const ExpertArgs a, int nslices,
-                                                        int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t ldw[2][kTBK * kDnWRow];
-  __shared__ __attribute__((aligned(16))) uint8_t ldh[2][kTiledRows * kTRow];
-  const int lb = xcd_logical(blockIdx.x, nblocks);
-  const int slice = lb % nslices;
-  TileInfo ti;
-  if (!decode_tile(a, lb / nslices, ti)) return;
+// down: block = 128 tokens x 512 output columns; wave w = 128 columns x 128
+// tokens.  Stage: 32 W_down rows i (1 KiB = 512 columns each) then the 128
+// hidden rows.  Lane (r16, q) reads 8 consecutive h at the 8 rows 8q..8q+7
+// and transposes the 8x8 block in registers: virtual tile j has row m at
+// h = 128 w + 8 m + j.
+template <bool FULL>
+__device__ __forceinline__ void down_tile(const ExpertArgs& a, const TileInfo& ti, int slice,
+                                          uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3) {
   const int I = ti.shared ? a.Is : a.I;
   const int H = a.H;
-  const int h0 = slice * kDnCols;
-  if (h0 >= H) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r16 = lane & 15;
-  const int wh = wave & 1, wt = wave >> 1;
+  const int hb = slice * kDnCols;       // first column of the block
+  const int h0 = hb + 128 * wave;       // first column of this wave
+  const bool wact = h0 < H;
 
-  // W_down staging: row (i) tid >> 3 of the 32-deep slice, 16-byte columns (tid & 7) + 8u
-  const int wr = tid >> 3, wc = tid & 7;
+  // load g < 8: W_down row k0 + 4 g + w, columns hb + 8 lane .. + 7 (clamped);
+  // loads 8, 9: hidden rows.  Byte offsets are fixed, the bases advance.
   const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
-  const uint16_t* wd = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_down : a.w_down) + ebase +
-                       (size_t)wr * H + h0 + wc * 8;
-  // hidden-row staging: rows (tid >> 2) + 64u, 16-byte column tid & 3
-  const int hr = tid >> 2, hc = tid & 3;
-  const uint16_t* hsrc = reinterpret_cast<const uint16_t*>(ti.shared ? a.h_shared : a.h_routed);
-  const uint16_t* hp[2];
+  const int ck = chunk_of(lane);
+  const int hcol = min(hb + 8 * lane, H - 8);
+  uint32_t off[kDmaPerWave];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = u * 64 + hr;
-    hp[u] = row < ti.nrows ? hsrc + (size_t)(ti.row0 + row) * I + hc * 8 : nullptr;
+  for (int j = 0; j < 8; ++j) off[j] = (uint32_t)(((size_t)(4 * j + wave) * H + hcol) * 2);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int row = token_row_of(8 + j, wave, lane);
+    if (row >= ti.nrows) row = 0;
+    off[8 + j] = (uint32_t)(((size_t)(ti.row0 + row) * I + ck * 8) * 2);
   }
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 sa[6], sb[6];
-  auto gload = [&](u32x4 (&st)[6], int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) st[u] = ld16(wd + (size_t)k0 * H + u * 64);
-    st[4] = hp[0] ? ld16(hp[0] + k0) : zero4;
-    st[5] = hp[1] ? ld16(hp[1] + k0) : zero4;
+  const uint16_t* wp = reinterpret_cast<const uint16_t*>(ti.shared ? a.ws_down : a.w_down) + ebase;
+  const uint16_t* hp = reinterpret_cast<const uint16_t*>(ti.shared ? a.h_shared : a.h_routed);
+  auto dma = [&](uint8_t* st) {
+    const void* base[kDmaPerWave] = {wp, wp, wp, wp, wp, wp, wp, wp, hp, hp};
+    dma_stage(base, off, wave_slot(st, wave));
+    wp += (size_t)kTBK * H;
+    hp += kTBK;
   };
-  auto sstore = [&](const u32x4 (&st)[6], int stage) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) st16(ldw[stage] + wr * kDnWRow + (wc + 8 * u) * 16, st[u]);
-    st16(ldh[stage] + swz(hr, hc), st[4]);
-    st16(ldh[stage] + swz(64 + hr, hc), st[5]);
-  };
-  const int wrows = ti.nrows - wt * 64;
-  f32x4 acc[8][4];
+
+  f32x4 acc[8][8];  // [virtual tile j][token sub-tile n]
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 8; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nsub = (ti.nrows + 15) >> 4;
 
-  auto compute = [&](int stage) {
-    u32x4 v[8], am[8], B[4];
-    const uint8_t* wb = ldw[stage] + (wh * 128 + 8 * r16) * 2;
+  // W row 4 j + w of the stage sits at LDS row 4 j + w, i.e. row i at i * 1 KiB.
+  // read() fetches the raw 8x8 blocks; the first half of mfma() transposes them.
+  u32x4 V[2][8], B[2][8], am[8];
+  auto read = [&](const uint8_t* st, int set) {
+    if (!wact) return;
+    const uint8_t* wb = st + 256 * wave + 16 * r16;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = lds16(wb + (q * 8 + r) * kDnWRow);
+    for (int t = 0; t < 2; ++t) {
+      if (t != set) continue;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) B[n] = lds16(ldh[stage] + swz(wt * 64 + n * 16 + r16, q));
-    transpose8x8(v, am);
+      for (int r = 0; r < 8; ++r) V[t][r] = lds16(wb + (8 * q + r) * 1024);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (n * 16 < wrows) {
+      for (int n = 0; n < 8; ++n)
+        if (FULL || n < nsub) B[t][n] = lds16(st + kTokOff + swz(16 * n + r16, q));
+    }
+  };
+  auto mfma = [&](int set, int half) {
+    if (!wact) return;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j][n] = mfma16x16x32(am[j], B[n], acc[j][n]);
+    for (int t = 0; t < 2; ++t) {
+      if (t != set) continue;
+      if (half == 0) transpose8x8(V[t], am);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h != half) continue;
+#pragma unroll
+        for (int n = 4 * h; n < 4 * h + 4; ++n) {
+          if (FULL || n < nsub) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j][n] = mfma16x16x32(am[j], B[t][n], acc[j][n]);
+          }
+        }
       }
     }
   };
 
-  const int nk = I / kTBK;
-  gload(sa, 0);
-  if (nk > 1) gload(sb, kTBK);
-  sstore(sa, 0);
-  __syncthreads();
-  for (int c = 0; c < nk; c += 2) {
-    if (c + 2 < nk) gload(sa, (c + 2) * kTBK);
-    compute(0);
-    if (c + 1 < nk) sstore(sb, 1);
-    __syncthreads();
-    if (c + 1 >= nk) break;
-    if (c + 3 < nk) gload(sb, (c + 3) * kTBK);
-    compute(1);
-    if (c + 2 < nk) sstore(sa, 0);
-    __syncthreads();
-  }
+  run_ring(I / kTBK, s0, s1, s2, s3, dma, read, mfma);
+  if (!wact) return;
 
-  // epilogue: tile j, C row 4q+i -> h = h0 + 128 wh + 8 (4q + i) + j
+  // epilogue: tile j, C row 4q + i -> h = h0 + 8 (4q + i) + j: 8 consecutive h
   uint16_t* obase = reinterpret_cast<uint16_t*>(ti.shared ? a.o_shared : a.o_routed);
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int row = wt * 64 + n * 16 + r16;
+  for (int n = 0; n < 8; ++n) {
+    const int row = 16 * n + r16;
     if (row < ti.nrows) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -273,10 +385,25 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(const ExpertArgs a, int n
         pk.y = pack_bf16x2(acc[2][n][i], acc[3][n][i]);
         pk.z = pack_bf16x2(acc[4][n][i], acc[5][n][i]);
         pk.w = pack_bf16x2(acc[6][n][i], acc[7][n][i]);
-        st16(obase + (size_t)(ti.row0 + row) * H + h0 + wh * 128 + 8 * (4 * q + i), pk);
+        st16(obase + (size_t)(ti.row0 + row) * H + h0 + 8 * (4 * q + i), pk);
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256, 1) void k_down_tiled(const ExpertArgs a, int nslices,
+                                                        int nblocks) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s3[kStageB];
+  const int lb = xcd_logical(blockIdx.x, nblocks);
+  const int slice = lb % nslices;
+  TileInfo ti;
+  if (!decode_tile(a, lb / nslices, ti)) return;
+  if (slice * kDnCols >= a.H) return;
+  if (ti.nrows == kTiledRows) down_tile<true>(a, ti, slice, s0, s1, s2, s3);
+  else down_tile<false>(a, ti, slice, s0, s1, s2, s3);
 }
 
 hipError_t launch_experts_tiled_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
@@ -286,19 +413,24 @@ hipError_t launch_experts_tiled_bf16(const ExpertArgs& a, hipStream_t s, const S
     stage_end(tm, kTiles, s);
     if (e != hipSuccess) return e;
   }
+  // the ring runs whole groups of four 32-deep stages
+  if (a.H % (4 * kTBK) != 0 || a.I % (4 * kTBK) != 0 || a.Is % (4 * kTBK) != 0 || a.H < 8)
+    return hipErrorInvalidValue;
   const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
   const int imax = a.I > a.Is ? a.I : a.Is;
-  const int gu_slices = (imax + 127) / 128;
+  const int gu_slices = (imax + kGuFeat - 1) / kGuFeat;
   int64_t nb = tiles * gu_slices;
   nb = (nb + 7) / 8 * 8;
   stage_begin(tm, kGateUp, s);
-  hipLaunchKernelGGL(k_gateup_tiled, dim3((unsigned)nb), dim3(256), 0, s, a, gu_slices, (int)nb);
+  hipLaunchKernelGGL(k_gateup_tiled, dim3((unsigned)nb), dim3(256), 0, s, a, gu_slices,
+                     (int)nb);
   stage_end(tm, kGateUp, s);
   const int dn_slices = (a.H + kDnCols - 1) / kDnCols;
   nb = tiles * dn_slices;
   nb = (nb + 7) / 8 * 8;
   stage_begin(tm, kDown, s);
-  hipLaunchKernelGGL(k_down_tiled, dim3((unsigned)nb), dim3(256), 0, s, a, dn_slices, (int)nb);
+  hipLaunchKernelGGL(k_down_tiled, dim3((unsigned)nb), dim3(256), 0, s, a, dn_slices,
+                     (int)nb);
   stage_end(tm, kDown, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -10,7 +10,7 @@ namespace moe {
 constexpr int kTileRows = 32;    // token rows per tile of the weight-streaming kernels
 constexpr int kTiledRows = 128;  // token rows per tile of the LDS-tiled kernels
 // Rows per expert tile for a layer: many rows per expert -> LDS-tiled GEMMs.
-int expert_tile_rows(int64_t T, int K, int E, int I, int Is, bool bf16);
+int expert_tile_rows(int64_t T, int K, int E, int I, int Is, int H, bool bf16);
 
 // Optional event pair around one kernel stage (see moe_layer_forward_timed).
 struct StageTimer {
