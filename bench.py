@@ -93,7 +93,8 @@ def measured_traffic(workload, kernel):
         return None
     csrc = os.path.join(ROOT, "group_limited_top_amd", "csrc")
     src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                   for f in ("experts.hip", "device.h", "kernels.h"))
+                   for f in ("experts.hip", "experts_tiled.hip", "expert_tiles.h", "device.h",
+                             "kernels.h"))
     if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
@@ -221,7 +222,7 @@ def main():
         achieved = work["k_gate_up"] / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    kname = "k_gateup_bf16" if shape.dtype == "bf16" else "k_gateup_f32"
+    kname = L.moe_stage_kernel(d, stage)
     roof["traffic"] = measured_traffic(shape.name, kname)
     roof.update(kernel=kname,
                 kernel_ms=round(kern_ms, 4), algorithmic_bytes=work["k_gate_up"],

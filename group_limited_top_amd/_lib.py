@@ -24,7 +24,7 @@ MOE_STATUS_NONFINITE, MOE_STATUS_BAD_INDEX = 1, 2
 EXPORTS = (
     "moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_layer_forward",
     "moe_residual_rmsnorm", "moe_status", "moe_sigmoid32", "moe_strerror",
-    "moe_layer_forward_timed",
+    "moe_layer_forward_timed", "moe_stage_kernel",
 )
 # kernel stages (moe_stage_t), in launch order
 STAGES = ("router_split", "logits", "select", "hist", "scan", "scatter", "tiles", "gate_up",
@@ -80,6 +80,8 @@ def _load():
     lib.moe_status.restype = i
     lib.moe_sigmoid32.argtypes = [P, P, ctypes.c_int64, P]
     lib.moe_sigmoid32.restype = i
+    lib.moe_stage_kernel.argtypes = [D, i]
+    lib.moe_stage_kernel.restype = ctypes.c_char_p
     lib.moe_strerror.argtypes = [i]
     lib.moe_strerror.restype = ctypes.c_char_p
     return lib
@@ -275,6 +277,13 @@ def moe_residual_rmsnorm(d: MoeDesc, x_in, y, x_out, r_out, eps: float = 1e-6, s
     )
     _rc(LIB.moe_residual_rmsnorm(ctypes.byref(d), *args, ctypes.c_float(eps), _stream(stream)),
         "moe_residual_rmsnorm")
+
+
+def moe_stage_kernel(d: MoeDesc, stage: str):
+    """Name of the kernel moe_layer_forward launches for an expert stage
+    ("gate_up", "down", "combine") with this desc, or None."""
+    r = LIB.moe_stage_kernel(ctypes.byref(d), STAGES.index(stage))
+    return None if r is None else r.decode()
 
 
 def moe_status(ws, stream=None) -> int:

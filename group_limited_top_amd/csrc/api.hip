@@ -314,6 +314,13 @@ int moe_layer_forward_timed(const moe_desc_t* desc, const void* x, const moe_wei
                        tracking, ws, ws_bytes, stream, &tm);
 }
 
+const char* moe_stage_kernel(const moe_desc_t* desc, int stage) {
+  if (validate(desc) != MOE_OK || desc->T == 0) return nullptr;
+  const moe_desc_t& d = *desc;
+  return moe::expert_stage_kernel(stage, d.T, d.top_k, d.E, d.I, d.I_shared, d.H,
+                                  d.dtype == MOE_BF16);
+}
+
 int moe_residual_rmsnorm(const moe_desc_t* desc, const void* x_in, const void* y, void* x_out,
                          void* r_out, float eps, hipStream_t stream) {
   int rc = validate(desc);

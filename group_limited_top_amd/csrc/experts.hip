@@ -338,10 +338,15 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
   }
   const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
   const int imax = a.I > a.Is ? a.I : a.Is;
-  const int slices = imax / 64;
-  stage_begin(tm, kGateUp, s);
-  hipLaunchKernelGGL(k_gateup_bf16, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
-  stage_end(tm, kGateUp, s);
+  if (stream_ring_ok(a)) {
+    const hipError_t e = launch_gateup_stream_bf16(a, tiles, s, tm);
+    if (e != hipSuccess) return e;
+  } else {
+    const int slices = imax / 64;
+    stage_begin(tm, kGateUp, s);
+    hipLaunchKernelGGL(k_gateup_bf16, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
+    stage_end(tm, kGateUp, s);
+  }
   const int hslices = (a.H + 511) / 512;
   const size_t lds = (size_t)kTileRows * (imax / 8 + 1) * 16;
   stage_begin(tm, kDown, s);
@@ -350,6 +355,29 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine_bf16(a, s, tm);
+}
+
+const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int Is, int H,
+                                bool bf16) {
+  const bool tiled = expert_tile_rows(T, K, E, I, Is, H, bf16) == kTiledRows;
+  ExpertArgs a{};
+  a.T = (int)T;
+  a.H = H;
+  a.E = E;
+  a.K = K;
+  a.I = I;
+  a.Is = Is;
+  switch (stage) {
+    case kGateUp:
+      if (!bf16) return "k_gateup_f32";
+      if (tiled) return "k_gateup_tiled";
+      return stream_ring_ok(a) ? "k_gateup_stream" : "k_gateup_bf16";
+    case kDown:
+      if (!bf16) return "k_down_f32";
+      return tiled ? "k_down_tiled" : "k_down_bf16";
+    case kCombine: return bf16 ? "k_combine_bf16" : "k_combine_f32";
+    default: return nullptr;
+  }
 }
 
 hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {

@@ -75,9 +75,16 @@ struct ExpertArgs {
 };
 int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows);
 hipError_t launch_experts_tiled_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
+// gate/up weight streaming through the LDS ring (32-row tiles); usable when stream_ring_ok.
+bool stream_ring_ok(const ExpertArgs& a);
+hipError_t launch_gateup_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,
+                                     const StageTimer* tm);
 hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm = nullptr);
 hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTimer* tm = nullptr);
+// Name of the kernel an expert stage (kGateUp, kDown, kCombine) launches for
+// this shape; nullptr for other stages.
+const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int Is, int H, bool bf16);
 
 // Residual + RMSNorm ----------------------------------------------------------
 hipError_t launch_residual_rmsnorm(bool bf16, const void* x_in, const void* y, void* x_out,

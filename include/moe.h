@@ -194,6 +194,12 @@ int moe_layer_forward_timed(const moe_desc_t* desc, const void* x, const moe_wei
                             int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
                             hipStream_t stream, int stage, hipEvent_t start, hipEvent_t stop);
 
+/* Name of the kernel that moe_layer_forward launches for `stage` with this
+ * desc, for the expert stages (MOE_STAGE_GATE_UP, _DOWN, _COMBINE), e.g.
+ * "k_gateup_stream"; NULL for other stages or an invalid desc.  Host only; the
+ * string is static.  For labelling measurements. */
+const char* moe_stage_kernel(const moe_desc_t* desc, int stage);
+
 /* Synchronises `stream`, then reads the workspace status word (MOE_STATUS_*)
  * into *status (host) and clears it. */
 int moe_status(void* ws, size_t ws_bytes, hipStream_t stream, uint32_t* status);
