@@ -27,6 +27,7 @@ struct Layout {
   size_t pair_slot;    // int32 [P]
   size_t perm;         // int32 permute scratch (large P only)
   size_t tile_off;     // int32 [E+2]
+  size_t tile_tab;     // int32 [max tiles][2]
   size_t h_routed;     // dtype [P][I]
   size_t h_shared;     // dtype [T][Is]
   size_t o_routed;     // dtype [P][H]
@@ -59,8 +60,13 @@ Layout make_layout(const moe_desc_t& d) {
   L.pair_slot = take(P * 4);
   L.perm = take(moe::permute_scratch_ints((int64_t)P, d.E) * 4);
   L.tile_off = take((E + 2) * 4);
-  L.h_routed = take(P * (size_t)d.I * elt);
-  L.h_shared = take(T * Is * elt);
+  L.tile_tab = take((size_t)moe::max_expert_tiles(d.T, d.top_k, d.E, d.I_shared,
+                                                  moe::expert_tile_rows(d.T, d.top_k, d.E, d.I,
+                                                                        d.I_shared, d.H, bf16)) *
+                    8);
+  // h rows are padded by one GEMM row tile (its loads may run past the last row)
+  L.h_routed = take((P + moe::kGRows) * (size_t)d.I * elt);
+  L.h_shared = take((T + moe::kGRows) * Is * elt);
   L.o_routed = take(P * H * elt);
   L.o_shared = take(Is > 0 ? T * H * elt : 0);
   L.total = o;
@@ -153,7 +159,7 @@ int run_permute(const moe_desc_t& d, const int32_t* idx, int32_t* counts, int32_
   return hip_rc(moe::launch_permute(idx, (int64_t)d.T * d.top_k, d.E, d.T, d.I_shared,
                                     tile_rows(d), at<int32_t>(ws, L.perm), counts, offsets, sorted_pair,
                                     pair_slot, tracking, at<int32_t>(ws, L.tile_off),
-                                    at<uint32_t>(ws, L.status), s, tm));
+                                    at<int32_t>(ws, L.tile_tab), at<uint32_t>(ws, L.status), s, tm));
 }
 
 int run_experts(const moe_desc_t& d, const void* x, const float* topk_w, const int32_t* offsets,
@@ -181,6 +187,7 @@ int run_experts(const moe_desc_t& d, const void* x, const float* topk_w, const i
   a.ws_down = W.ws_down;
   a.y = y;
   a.tile_off = at<int32_t>(ws, L.tile_off);
+  a.tile_tab = at<int32_t>(ws, L.tile_tab);
   a.tiles_ready = tiles_ready;
   a.tile_rows = tile_rows(d);
   a.h_routed = at<void>(ws, L.h_routed);

@@ -31,7 +31,18 @@ __device__ __forceinline__ bool decode_tile(const ExpertArgs& a, int tile, TileI
   return true;
 }
 
-// Builds tile_off from offsets (used when the permute kernels did not).
+// Tile table entry t (two int32): {e | nrows << 16, row0}: expert (E = the
+// shared expert), rows in the tile, first row (expert-sorted pair row, or
+// token for the shared expert).
+__device__ __forceinline__ void write_tile_entry(int32_t* tab, int32_t t, int e, int32_t first,
+                                                 int32_t rows, int32_t m, int tile_rows) {
+  const int32_t row0 = first + m * tile_rows;
+  const int32_t nrows = min(tile_rows, rows - m * tile_rows);
+  tab[2 * t] = e | (nrows << 16);
+  tab[2 * t + 1] = row0;
+}
+
+// Builds tile_off and tile_tab from offsets (used when the permute kernels did not).
 hipError_t launch_tiles(const ExpertArgs& a, hipStream_t s);
 
 }  // namespace moe

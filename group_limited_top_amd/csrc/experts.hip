@@ -34,27 +34,31 @@ int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows) {
   return n;
 }
 
-// Few rows per expert (on average fewer than kTiledRows / 2): stream each
-// expert's weights once past its rows; otherwise run the LDS-pipelined GEMMs
-// (bf16, feature sizes in whole 128-wide slices, token and hidden arrays
-// addressable with 32-bit byte offsets).
+// Few rows per expert (on average fewer than kGRows / 2): stream each
+// expert's weights once past its rows; otherwise run the LDS-pipelined MFMA
+// GEMMs (bf16, shapes with gemm_shape_ok).
 int expert_tile_rows(int64_t T, int K, int E, int I, int Is, int H, bool bf16) {
-  const int64_t imax = I > Is ? I : Is;
-  const bool tiled_ok = bf16 && I % 128 == 0 && Is % 128 == 0 && H % 128 == 0 &&
-                        T * H * 2 < (int64_t(1) << 32) && T * K * imax * 2 < (int64_t(1) << 32);
-  return (tiled_ok && (T * K) / E >= kTiledRows / 2) ? kTiledRows : kTileRows;
+  return (bf16 && gemm_shape_ok(T, K, I, Is, H) && (T * K) / E >= kGRows / 2) ? kGRows : kTileRows;
 }
 
 // tile_off[g] = number of tiles of "experts" 0..g-1 (E + 1 of them, the last
-// is the shared expert with T rows when Is > 0); tile_off[E + 1] = total.
+// is the shared expert with T rows when Is > 0); tile_off[E + 1] = total;
+// tile_tab = one entry per tile (write_tile_entry).
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offsets, int E, int T,
                                                  int Is, int tile_rows,
-                                                 int32_t* __restrict__ tile_off) {
+                                                 int32_t* __restrict__ tile_off,
+                                                 int32_t* __restrict__ tile_tab) {
   __shared__ int32_t sc[1024];
   const int g = threadIdx.x;
-  int32_t n = 0;
-  if (g < E) n = (offsets[g + 1] - offsets[g] + tile_rows - 1) / tile_rows;
-  else if (g == E && Is > 0) n = (T + tile_rows - 1) / tile_rows;
+  int32_t n = 0, rows = 0, first = 0;
+  if (g < E) {
+    first = offsets[g];
+    rows = offsets[g + 1] - first;
+    n = (rows + tile_rows - 1) / tile_rows;
+  } else if (g == E && Is > 0) {
+    rows = T;
+    n = (T + tile_rows - 1) / tile_rows;
+  }
   sc[g] = n;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
@@ -65,11 +69,12 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offs
   }
   if (g <= E) tile_off[g] = sc[g] - n;
   if (g == E) tile_off[E + 1] = sc[g];
+  for (int32_t m = 0; m < n; ++m) write_tile_entry(tile_tab, sc[g] - n + m, g, first, rows, m, tile_rows);
 }
 
 hipError_t launch_tiles(const ExpertArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is, a.tile_rows,
-                     a.tile_off);
+                     a.tile_off, a.tile_tab);
   return hipGetLastError();
 }
 
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
 }
 
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
-  if (a.tile_rows == kTiledRows) return launch_experts_tiled_bf16(a, s, tm);
+  if (a.tile_rows == kGRows) return launch_experts_gemm_bf16(a, s, tm);
   // the down kernel's LDS tile can exceed the 64 KiB default for I > 960
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k_down_bf16), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -359,7 +364,7 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
 
 const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int Is, int H,
                                 bool bf16) {
-  const bool tiled = expert_tile_rows(T, K, E, I, Is, H, bf16) == kTiledRows;
+  const bool tiled = expert_tile_rows(T, K, E, I, Is, H, bf16) == kGRows;
   ExpertArgs a{};
   a.T = (int)T;
   a.H = H;
@@ -370,11 +375,11 @@ const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int I
   switch (stage) {
     case kGateUp:
       if (!bf16) return "k_gateup_f32";
-      if (tiled) return "k_gateup_tiled";
+      if (tiled) return "k_expert_gemm<0>";
       return stream_ring_ok(a) ? "k_gateup_stream" : "k_gateup_bf16";
     case kDown:
       if (!bf16) return "k_down_f32";
-      return tiled ? "k_down_tiled" : "k_down_bf16";
+      return tiled ? "k_expert_gemm<1>" : "k_down_bf16";
     case kCombine: return bf16 ? "k_combine_bf16" : "k_combine_f32";
     default: return nullptr;
   }

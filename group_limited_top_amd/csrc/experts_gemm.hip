@@ -1,0 +1,498 @@
+// experts_gemm.hip -- MFMA grouped GEMMs of the experts for many rows per
+// expert (a large batch of tokens).
+//
+// [Routing §四]: every expert is down(silu(gate x) * up x) over stacked
+// [E][I][H] weights; [Routing §五]: the shared expert is one more bucket (all T
+// tokens).  Rows are the expert-sorted pairs; a row tile is kGRows rows of one
+// expert (the tile table, see write_tile_entry).
+//
+// Block: 8 waves (two per SIMD), a 256 x 256 output tile; wave w = (wm, wn)
+// = (w / 2, w % 2) owns 64 token rows (64 wm..) x 128 columns, 8 x 4 MFMA
+// 16x16x32 tiles (128 accumulators per lane).  The two waves of a SIMD
+// (w, w + 4) have different rows, so a tile with at most 128 rows still
+// keeps every SIMD busy.
+//   gate/up: columns = 128 gate + 128 up weight rows (features i0..i0+127);
+//            wave (wm, wn) owns features 64 wn.. of both gate and up, so
+//            h = silu(g) * u is formed in registers.  K = H.
+//   down:    rows = h rows (contiguous), columns = 256 outputs; W_down[e] is
+//            [I][H] (H contiguous), and the LDS transpose read
+//            (ds_read_b64_tr_b16) turns its staged [k][column] rows into the
+//            MFMA operand (4 consecutive k of one column per lane).  K = I.
+//
+// Data path.  A step is 64 deep in K, so every staged row is one whole
+// 128-byte line (half lines halve what the load path delivers per CU).  The
+// operands of a step are two 32 KiB slices (tokens, weights) staged by direct
+// global -> LDS loads (global_load_lds_dwordx4: 1 KiB per wave instruction);
+// five slice buffers (160 KiB, all of the CU's LDS) form a ring, so while a
+// step is computed the next one and a half steps are in flight.  Operands go
+// from LDS to registers one 32-deep half step ahead of the MFMAs that use
+// them (two register sets).
+//
+// Blocks are persistent (one per CU) and walk a static list of tiles, the
+// ring running on from one tile into the next.  Tiles are ordered expert by
+// expert; XCD x (blocks b with b mod 8 = x) takes the x-th eighth of the list
+// and its blocks interleave over it, so the blocks of one XCD work on the same
+// few experts at a time and share their weights and token rows in its L2.
+#include "device.h"
+#include "expert_tiles.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kGK = 64;           // K depth of a step
+constexpr int kSliceB = 32768;    // bytes of one staged slice
+constexpr int kRingN = 5;         // slice buffers in the ring
+constexpr int kGuFeat = 128;      // h features per gate/up tile
+constexpr int kDnOut = 256;       // output columns per down tile
+
+typedef __attribute__((address_space(3))) const void lvoid_t;
+
+// Scalar (wave-uniform) load through the constant address space.
+__device__ __forceinline__ int32_t sload(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// One slice's 4 loads of this wave: load j brings the lane's 16 bytes from
+// base + off[j] into LDS lds + 1 KiB j + 16 lane.  M0 (the LDS destination) is
+// saved and restored around the loads, and every write of M0 is followed by
+// the one wait state an LDS DMA reading M0 needs after a scalar write of it.
+// Inline asm keeps the compiler from tying later LDS reads to these loads; the
+// ring orders them (ring_wait).  The memory clobber keeps LDS accesses in
+// place around it.
+__device__ __forceinline__ void dma4(const void* base_, const uint32_t (&off)[4], uint32_t lds) {
+  // the base is wave-uniform; readfirstlane makes that visible (its result
+  // is a signed int: widen each half as unsigned)
+  const uint64_t b = reinterpret_cast<uint64_t>(base_);
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const void* base = reinterpret_cast<const void*>(((uint64_t)bhi << 32) | (uint64_t)blo);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\ts_add_u32 m0, m0, 1024\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\ts_add_u32 m0, m0, 1024\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\ts_add_u32 m0, m0, 1024\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base), "s"(lds)
+      : "memory", "scc");
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and its LDS reads are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void ring_wait() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Row slices (256 rows x 128 B): 16-byte chunk c of row r sits at
+// r * 128 + 16 (c ^ ((r >> 1) & 7)), so that 16 consecutive rows read at one
+// chunk index cover all 64 banks.  A DMA load j of wave w writes rows
+// 32 w + 8 j + lane / 8, slot lane & 7, i.e. logical chunk rs_chunk(j, lane).
+__device__ __forceinline__ int rs_addr(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int rs_chunk(int j, int lane) { return (lane & 7) ^ ((4 * j + (lane >> 4)) & 7); }
+
+__device__ __forceinline__ u32x4 lds16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// W_down slices (64 rows k x 512 B): 16-byte chunk c of row r sits at chunk
+// c ^ wd_swz(r).  The transpose reads of one instruction cover 16 rows
+// (8 q + c, q, c = 0..3) at one 32-byte column window; the XOR spreads them
+// over the 8 windows of a 256-byte bank line, two rows each.
+__device__ __forceinline__ int wd_swz(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
+
+// LDS transpose read: within each group of 16 lanes, lane i receives element
+// (i & 3) of the 4 x 16-bit values addressed by lane 4 c + (i >> 2), for
+// c = 0..3.  So if lane 4 c + m of a group points at row c, columns 4 m..4 m + 3
+// of a [k][column] block, lane i gets column i at rows 0..3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) uint8_t*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+struct GTile {
+  int e, row0, nrows, s;  // expert (E = shared), first row, rows, column slice
+};
+
+// Tile t of the list: row tile t / S, column slice t % S.  Everything here is
+// wave-uniform; readfirstlane keeps it in scalar registers, so the table is
+// read with scalar loads (a vector load would make the compiler wait for all
+// vector-memory operations in flight, the ring's loads included).
+__device__ __forceinline__ GTile gtile(const int32_t* tab, int t, int S) {
+  t = __builtin_amdgcn_readfirstlane(t);
+  const int rt = t / S;
+  GTile g;
+  const int32_t v = __builtin_amdgcn_readfirstlane(sload(tab + 2 * rt));
+  g.e = v & 0xffff;
+  g.nrows = v >> 16;
+  g.row0 = __builtin_amdgcn_readfirstlane(sload(tab + 2 * rt + 1));
+  g.s = t - rt * S;
+  return g;
+}
+
+// A wave-uniform pointer, made visible as such.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// 8-byte store to global memory (a global, not flat, store: flat stores would
+// also count against the LDS counter the ring waits on).  Plain stores: the
+// streaming (nontemporal) kind measured much slower for the down outputs.
+__device__ __forceinline__ void store8(uint16_t* p, u32x2 v) {
+  *(__attribute__((address_space(1))) u32x2*)p = v;
+}
+
+// Vector load of one int32 issued as inline asm: the compiler then inserts no
+// wait for it (which would also wait for the ring's loads).  The caller reads
+// the value only after later ring waits have covered it, and passes it through
+// settle() there so that the read cannot move above them.
+__device__ __forceinline__ int32_t load_i32_async(const int32_t* p) {
+  int32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void settle(int32_t& v) { asm volatile("" : "+v"(v)); }
+
+// MODE 0: gate/up + SwiGLU; MODE 1: down.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int S) {
+  constexpr int kStores = MODE == 0 ? 16 : 32;  // epilogue stores per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingN * kSliceB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int H = a.H, I = a.I, E = a.E;
+  // the operand arrays, read once from the kernel arguments into scalar
+  // registers (selecting among struct fields later would otherwise become a
+  // vector load of the argument block)
+  const uint8_t* const x_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.x));
+  const uint8_t* const hr_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.h_routed));
+  const uint8_t* const hs_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.h_shared));
+  const uint16_t* const wg_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_gate));
+  const uint16_t* const wu_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_up));
+  const uint16_t* const wd_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_down));
+  const uint16_t* const sg_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_gate));
+  const uint16_t* const su_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_up));
+  const uint16_t* const sd_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_down));
+  const int32_t* const sp_p = uniform_ptr(a.sorted_pair);
+  uint16_t* const hrw_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.h_routed));
+  uint16_t* const orw_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.o_routed));
+  uint16_t* const osw_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.o_shared));
+  const int T = a.T, K = a.K;
+  const int32_t* const tab_p = uniform_ptr(a.tile_tab);
+  const int32_t* const toff_p = uniform_ptr(a.tile_off);
+  // (the argument block is not touched below: a use after one of the inline
+  // asm statements, which clobber memory, would keep a private copy of it)
+  // Shared-expert arrays as offsets from the routed ones: the lambdas below
+  // then pick with an integer select (a select between two captured pointers
+  // would become a load through a select of their addresses, which keeps
+  // them in private memory).
+  const uint16_t* const wgu_p = w < 4 ? wg_p : wu_p;            // this wave's gate or up
+  const ptrdiff_t sh_wgu = (w < 4 ? sg_p : su_p) - wgu_p;        // shared minus routed
+  const ptrdiff_t sh_wd = sd_p - wd_p;
+  const ptrdiff_t sh_h = hs_p - hr_p;   // bytes
+  const ptrdiff_t sh_hw = sh_h / 2;      // bf16 elements (both arrays are 256-byte aligned)
+  const ptrdiff_t sh_o = osw_p - orw_p;
+
+  // this block's tiles: first + m * nbx, m = 0 .. count - 1
+  const int ntiles = sload(toff_p + E + 1) * S;
+  const int nbx = (int)(gridDim.x >> 3);
+  const int x8 = (int)(blockIdx.x & 7);
+  const int lo = (int)((int64_t)ntiles * x8 / 8), hi = (int)((int64_t)ntiles * (x8 + 1) / 8);
+  const int first = lo + (int)(blockIdx.x >> 3);
+  if (first >= hi) return;
+  const int count = (hi - first + nbx - 1) / nbx;
+  const int nsteps = (MODE == 0 ? H : I) / kGK;
+  const int total = count * nsteps;  // steps of this block
+  const int nslices = 2 * total;     // slice 2s: token rows of step s, 2s + 1: weights
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lvoid_t*)ring)));
+
+  // ---- DMA ---------------------------------------------------------------
+  // token rows: this wave's loads j cover slice rows 32 w + 8 j + lane / 8
+  int xm = -1, xk = 0;          // tile (m) and step of the next token slice
+  const uint8_t* xb = nullptr;  // wave-uniform base of the current tile
+  uint32_t xo[4];               // lane offsets of the current tile
+  int32_t ptok[4];              // gate/up: sorted pairs of the next tile's rows
+  int pe = 0, prow0 = 0;
+  // weights
+  int wmi = -1, wk = 0;
+  const uint8_t* wb = nullptr;
+  uint32_t wo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (MODE == 0) {
+      // gate (w < 4) or up rows 32 (w & 3) + 8 j + lane / 8 of the tile's features
+      wo[j] = (uint32_t)((8 * j + (lane >> 3)) * H * 2 + rs_chunk(j, lane) * 16);
+    } else {
+      // W_down row r = 2 (4 w + j) + lane / 32 of the step; LDS slot lane & 31
+      // holds logical chunk (lane & 31) ^ wd_swz(r)
+      const int r = 2 * (4 * w + j) + (lane >> 5);
+      wo[j] = (uint32_t)(r * H * 2 + (((lane & 31) ^ wd_swz(r)) * 16));
+    }
+    // down: h rows of the tile are contiguous (the buffers are padded by a
+    // whole tile, so rows past the tile's end are readable)
+    xo[j] = (uint32_t)((32 * w + 8 * j + (lane >> 3)) * I * 2 + rs_chunk(j, lane) * 16);
+  }
+  auto fetch_rows = [&](int t) __attribute__((always_inline)) {
+    const GTile g = gtile(tab_p, t, S);
+    pe = g.e;
+    prow0 = g.row0;
+    if (MODE == 0 && g.e < E) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ptok[j] = load_i32_async(sp_p + g.row0 +
+                                 min(32 * w + 8 * j + (lane >> 3), g.nrows - 1));
+    }
+  };
+  fetch_rows(first);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first tile's rows, before any ring load
+  auto issue_x = [&](uint32_t lds) __attribute__((always_inline)) {
+    if (xk == 0) {
+      ++xm;
+      if (MODE == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // ptok was loaded a whole tile (H / 64 >= 4 steps) ago: the ring
+          // waits since then, each leaving at most 4 + kStores loads
+          // outstanding while at least 8 were issued per step, have covered it
+          settle(ptok[j]);
+          const int tok = pe < E ? ptok[j] / K : prow0 + 32 * w + 8 * j + (lane >> 3);
+          xo[j] = (uint32_t)(min(tok, T - 1) * H * 2 + rs_chunk(j, lane) * 16);
+        }
+        xb = x_p;
+      } else {
+        xb = uniform_ptr(hr_p + (pe < E ? 0 : sh_h) + (size_t)prow0 * I * 2);
+      }
+      if (xm + 1 < count) fetch_rows(first + (xm + 1) * nbx);
+    }
+    dma4(xb + xk * 128, xo, lds);
+    if (++xk == nsteps) xk = 0;
+  };
+  auto issue_w = [&](uint32_t lds) __attribute__((always_inline)) {
+    if (wk == 0) {
+      ++wmi;
+      const GTile g = gtile(tab_p, first + wmi * nbx, S);
+      const bool sh = g.e >= E;
+      const size_t ebase = sh ? 0 : (size_t)g.e * I * H;
+      if (MODE == 0) {
+        const uint16_t* src = wgu_p + (sh ? sh_wgu : 0);
+        wb = uniform_ptr(reinterpret_cast<const uint8_t*>(
+            src + ebase + (size_t)(g.s * kGuFeat + 32 * (w & 3)) * H));
+      } else {
+        const uint16_t* src = wd_p + (sh ? sh_wd : 0);
+        wb = uniform_ptr(reinterpret_cast<const uint8_t*>(src + ebase + (size_t)g.s * kDnOut));
+      }
+    }
+    const size_t step_bytes = MODE == 0 ? 128 : (size_t)kGK * H * 2;
+    dma4(wb + wk * step_bytes, wo, lds);
+    if (++wk == nsteps) wk = 0;
+  };
+  // Slice sigma goes to buffer sigma % 5; slice 2 s holds the token rows of
+  // step s, slice 2 s + 1 its weights.  The prologue issues slices 0..4; step
+  // g then issues slice 2 g + 3 (weights of step g + 1) and 2 g + 4 (tokens of
+  // step g + 2), each cursor from one place.
+  auto slot = [&](int sigma) __attribute__((always_inline)) {
+    return ring0 + (uint32_t)((sigma % kRingN) * kSliceB) + 4096u * w;
+  };
+
+  // ---- compute -------------------------------------------------------------
+  f32x4 acc[8][4];  // [column tile i][row tile n]
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // lane parts of the LDS addresses of half step h; 16-row groups of a row
+  // slice are whole 2 KiB apart (the swizzle only sees a row's low bits)
+  // down: lane 4 c + m of group q reads row 32 h + 8 q + c (+ 4 for the
+  // second read) at columns 128 wn + 16 t + 4 m..+3 for A tile t, i.e. 16-byte
+  // chunk 16 wn + 2 t + m / 2, half m & 1.  Rows 32 h + 8 q + c and + 4 share
+  // their swizzle, so a lane's chunk for tile t is 16 wn + (dn_v ^ 2 t).
+  int lane_b[2], lane_a[2];
+  int dn_v = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    lane_b[h] = rs_addr(64 * wm + r16, 4 * h + q);
+    if (MODE == 0) {
+      lane_a[h] = rs_addr(64 * wn + r16, 4 * h + q);
+    } else {
+      const int r = 32 * h + 8 * q + (r16 >> 2);
+      lane_a[h] = r * 512 + 256 * wn + 8 * (r16 & 1);
+      dn_v = ((r16 & 3) >> 1) ^ wd_swz(r);
+    }
+  }
+  auto half_step = [&](int g, int h) __attribute__((always_inline)) {
+    const uint8_t* bx = ring + ((2 * g) % kRingN) * kSliceB + lane_b[h];
+    const uint8_t* bw = ring + ((2 * g + 1) % kRingN) * kSliceB + lane_a[h];
+    u32x4 A[8], B[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) B[n] = lds16(bx + 2048 * n);
+    if (MODE == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A[i] = lds16(bw + 2048 * i);
+        A[4 + i] = lds16(bw + 16384 + 2048 * i);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint8_t* p = bw + ((dn_v ^ (2 * t)) << 4);
+        const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 512);
+        A[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[i][n] = mfma16x16x32(A[i], B[n], acc[i][n]);
+  };
+  // Every epilogue issues the same number of stores per wave (kStores), rows
+  // past the tile's end going to trash (the padding rows of h_routed, whose
+  // contents are never used), so that the ring's waits can count them.
+  // Each lane has its own 8 bytes of trash (blocks spread over the padding
+  // rows), so the dropped stores do not all hit one line.
+  uint16_t* const trash = hrw_p + (size_t)T * K * I + (size_t)(blockIdx.x & 7) * 2048 + 4 * tid;
+  auto epilogue = [&](int m) __attribute__((always_inline)) {
+    const GTile g = gtile(tab_p, first + m * nbx, S);
+    const bool sh = g.e >= E;
+    const int rr = 64 * wm + r16;
+    if (MODE == 0) {
+      const int Iw = I;  // I == Is on this path
+      uint16_t* hb = hrw_p + (sh ? sh_hw : 0) +
+                     (size_t)(g.row0 + rr) * Iw + g.s * kGuFeat + 64 * wn + 4 * q;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bool ok = rr + 16 * n < g.nrows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float hv[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) hv[c] = silu_f32(acc[i][n][c]) * acc[4 + i][n][c];
+          u32x2 pk;
+          pk.x = pack_bf16x2(hv[0], hv[1]);
+          pk.y = pack_bf16x2(hv[2], hv[3]);
+          uint16_t* dst = ok ? hb + (size_t)16 * n * Iw + 16 * i : trash;
+          store8(dst, pk);
+        }
+      }
+    } else {
+      // tile t, C row 4 q + c: column 128 wn + 16 t + 4 q + c
+      uint16_t* ob = orw_p + (sh ? sh_o : 0) +
+                     (size_t)(g.row0 + rr) * H + g.s * kDnOut + 128 * wn + 4 * q;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bool ok = rr + 16 * n < g.nrows;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          u32x2 pk;
+          pk.x = pack_bf16x2(acc[t][n][0], acc[t][n][1]);
+          pk.y = pack_bf16x2(acc[t][n][2], acc[t][n][3]);
+          uint16_t* dst = ok ? ob + (size_t)16 * n * H + 16 * t : trash;
+          store8(dst, pk);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // Step g: wait until slices 2g, 2g + 1 have landed and every wave is done
+  // with step g - 1, refill step g - 1's buffers (slices up to 2g + 4), then
+  // compute.  Loads per wave per slice: 4.  A tile's epilogue runs in the next
+  // step, after that step's loads are issued: its stores are then younger than
+  // the slices the following wait needs (that wait lets them stay
+  // outstanding) and have until the wait after it to complete.
+  for (int sg = 0; sg < 2 && sg < total; ++sg) {
+    issue_x(slot(2 * sg));
+    issue_w(slot(2 * sg + 1));
+  }
+  if (2 < total) issue_x(slot(4));
+  int g = 0;
+  bool stored = false;  // the previous step issued an epilogue's stores
+  for (int cm = 0; cm < count; ++cm) {
+    const bool wact = 64 * wm < gtile(tab_p, first + cm * nbx, S).nrows;  // this wave has rows
+    for (int ck = 0; ck < nsteps; ++ck, ++g) {
+      // slices issued so far: min(2 total, max(5, 2 g + 3)); those after the
+      // two this step needs (2 g, 2 g + 1):
+      const int ahead = min(nslices, max(kRingN, 2 * g + 3)) - (2 * g + 2);
+      if (stored) {
+        if (ahead >= 1) ring_wait<4 + kStores>();
+        else ring_wait<kStores>();
+      } else {
+        if (ahead >= 3) ring_wait<12>();
+        else if (ahead == 2) ring_wait<8>();
+        else if (ahead == 1) ring_wait<4>();
+        else ring_wait<0>();
+      }
+      if (g >= 1 && g + 1 < total) issue_w(slot(2 * g + 3));
+      if (g >= 1 && g + 2 < total) issue_x(slot(2 * g + 4));
+      stored = ck == 0 && cm > 0;
+      if (stored) epilogue(cm - 1);
+      if (wact) {
+        half_step(g, 0);
+        half_step(g, 1);
+      }
+    }
+  }
+  epilogue(count - 1);
+}
+
+bool gemm_shape_ok(int64_t T, int K, int I, int Is, int H) {
+  // 128-feature gate/up and 256-column down slices, whole 64-deep steps, lane
+  // byte offsets below 2^31
+  return I == Is && I % kGuFeat == 0 && I % kGK == 0 && H % kDnOut == 0 && H % kGK == 0 &&
+         T * H * 2 < (int64_t(1) << 31) && T * K * I * 2 < (int64_t(1) << 31) &&
+         (int64_t)H * 2 * kGK < (int64_t(1) << 31);
+}
+
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
+  if (a.tile_rows != kGRows || !gemm_shape_ok(a.T, a.K, a.I, a.Is, a.H)) return hipErrorInvalidValue;
+  if (!a.tiles_ready) {
+    stage_begin(tm, kTiles, s);
+    const hipError_t e = launch_tiles(a, s);
+    stage_end(tm, kTiles, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
+  const int gu_slices = a.I / kGuFeat, dn_slices = a.H / kDnOut;
+  const int cus = cu_count() / 8 * 8;
+  auto grid = [&](int64_t tiles) __attribute__((always_inline)) {
+    int64_t g = tiles < cus ? (tiles + 7) / 8 * 8 : cus;
+    return dim3((unsigned)(g > 0 ? g : 8));
+  };
+  stage_begin(tm, kGateUp, s);
+  hipLaunchKernelGGL(k_expert_gemm<0>, grid(rtiles * gu_slices), dim3(512), 0, s, a, gu_slices);
+  stage_end(tm, kGateUp, s);
+  stage_begin(tm, kDown, s);
+  hipLaunchKernelGGL(k_expert_gemm<1>, grid(rtiles * dn_slices), dim3(512), 0, s, a, dn_slices);
+  stage_end(tm, kDown, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_combine_bf16(a, s, tm);
+}
+
+}  // namespace moe

@@ -8,8 +8,8 @@
 namespace moe {
 
 constexpr int kTileRows = 32;    // token rows per tile of the weight-streaming kernels
-constexpr int kTiledRows = 128;  // token rows per tile of the LDS-tiled kernels
-// Rows per expert tile for a layer: many rows per expert -> LDS-tiled GEMMs.
+constexpr int kGRows = 256;      // token rows per tile of the LDS-pipelined GEMMs
+// Rows per expert tile for a layer: many rows per expert -> LDS-pipelined GEMMs.
 int expert_tile_rows(int64_t T, int K, int E, int I, int Is, int H, bool bf16);
 
 // Optional event pair around one kernel stage (see moe_layer_forward_timed).
@@ -49,8 +49,8 @@ size_t permute_scratch_ints(int64_t P, int E);
 hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int tile_rows,
                           int32_t* scratch, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking,
-                          int32_t* tile_off, uint32_t* status, hipStream_t s,
-                          const StageTimer* tm = nullptr);
+                          int32_t* tile_off, int32_t* tile_tab, uint32_t* status,
+                          hipStream_t s, const StageTimer* tm = nullptr);
 
 // Experts ---------------------------------------------------------------------
 
@@ -66,7 +66,8 @@ struct ExpertArgs {
   void* y;
   // workspace
   int32_t* tile_off;  // [E+2]
-  int tile_rows;      // token rows per tile (kTileRows or kTiledRows)
+  int32_t* tile_tab;  // [max_expert_tiles][2] (see write_tile_entry)
+  int tile_rows;      // token rows per tile (kTileRows or kGRows)
   bool tiles_ready;   // tile_off already built (by the permute kernels)
   void* h_routed;     // [P][I]
   void* h_shared;     // [T][Is]
@@ -74,7 +75,9 @@ struct ExpertArgs {
   void* o_shared;     // [T][H]
 };
 int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows);
-hipError_t launch_experts_tiled_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
+// LDS-pipelined MFMA GEMMs (tile_rows == kGRows); shapes with gemm_shape_ok.
+bool gemm_shape_ok(int64_t T, int K, int I, int Is, int H);
+hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
 // gate/up weight streaming through the LDS ring (32-row tiles); usable when stream_ring_ok.
 bool stream_ring_ok(const ExpertArgs& a);
 hipError_t launch_gateup_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,

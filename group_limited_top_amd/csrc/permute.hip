@@ -17,6 +17,7 @@
 // An index outside [0, E) is skipped (not counted, pair_slot = -1) and sets
 // status bit 2.
 #include "device.h"
+#include "expert_tiles.h"
 #include "kernels.h"
 
 namespace moe {
@@ -60,12 +61,13 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* sc) {
   return r;
 }
 
-// counts/offsets/tracking/tile_off from per-expert totals held by thread e.
+// counts/offsets/tracking/tile_off/tile_tab from per-expert totals held by
+// thread e.
 __device__ __forceinline__ void finish_counts(int32_t total, int E, int T, int Is, int tile_rows,
                                               int32_t* sc,
                                               int32_t* counts, int32_t* offsets,
                                               int32_t* offs_lds, int64_t* tracking,
-                                              int32_t* tile_off) {
+                                              int32_t* tile_off, int32_t* tile_tab) {
   const int e = threadIdx.x;
   const int32_t incl = block_scan_1024(e < E ? total : 0, sc);
   if (e < E) {
@@ -82,6 +84,9 @@ __device__ __forceinline__ void finish_counts(int32_t total, int E, int T, int I
   const int32_t tin = block_scan_1024(n, sc);
   if (e <= E) tile_off[e] = tin - n;
   if (e == E) tile_off[E + 1] = tin;
+  const int32_t rows = e < E ? total : T;
+  const int32_t first = e < E ? incl - total : 0;
+  for (int32_t m = 0; m < n; ++m) write_tile_entry(tile_tab, tin - n + m, e, first, rows, m, tile_rows);
 }
 
 // ----------------------------------------------------------------------------
@@ -95,7 +100,8 @@ __global__ __launch_bounds__(1024) void k_permute_small(
     int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_slot, int64_t* __restrict__ tracking,
-    int32_t* __restrict__ tile_off, uint32_t* __restrict__ status) {
+    int32_t* __restrict__ tile_off, int32_t* __restrict__ tile_tab,
+    uint32_t* __restrict__ status) {
   __shared__ int32_t cnt[kSmallWaves][kPermMaxE];  // 32 KB
   __shared__ int32_t sc[1024];
   __shared__ int32_t offs[kPermMaxE];
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(1024) void k_permute_small(
       total += c;
     }
   }
-  finish_counts(total, E, T, Is, tile_rows, sc, counts, offsets, offs, tracking, tile_off);
+  finish_counts(total, E, T, Is, tile_rows, sc, counts, offsets, offs, tracking, tile_off, tile_tab);
   __syncthreads();
 #pragma unroll
   for (int b = 0; b < kSmallBatches; ++b) {
@@ -223,7 +229,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
                                                      int64_t* __restrict__ tracking,
-                                                     int32_t* __restrict__ tile_off) {
+                                                     int32_t* __restrict__ tile_off,
+                                                     int32_t* __restrict__ tile_tab) {
   __shared__ int32_t sc[1024];
   const int e = threadIdx.x;
   int32_t total = 0;
@@ -239,7 +246,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
       }
     }
   }
-  finish_counts(total, E, T, Is, tile_rows, sc, counts, offsets, nullptr, tracking, tile_off);
+  finish_counts(total, E, T, Is, tile_rows, sc, counts, offsets, nullptr, tracking, tile_off,
+                tile_tab);
 }
 
 __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ idx, int64_t P,
@@ -269,13 +277,13 @@ size_t permute_scratch_ints(int64_t P, int E) {
 hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, int tile_rows,
                           int32_t* scratch, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_slot, int64_t* tracking,
-                          int32_t* tile_off, uint32_t* status, hipStream_t s,
-                          const StageTimer* tm) {
+                          int32_t* tile_off, int32_t* tile_tab, uint32_t* status,
+                          hipStream_t s, const StageTimer* tm) {
   if (P <= kSmallMaxP) {
     stage_begin(tm, kHist, s);
     hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, s, idx, (int)P, E, T, Is,
                        tile_rows, counts, offsets, sorted_pair, pair_slot, tracking, tile_off,
-                       status);
+                       tile_tab, status);
     stage_end(tm, kHist, s);
     return hipGetLastError();
   }
@@ -290,7 +298,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int T, int Is, i
   stage_end(tm, kHist, s);
   stage_begin(tm, kScan, s);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E, T, Is, tile_rows,
-                     chunk_base, counts, offsets, tracking, tile_off);
+                     chunk_base, counts, offsets, tracking, tile_off, tile_tab);
   stage_end(tm, kScan, s);
   stage_begin(tm, kScatter, s);
   hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, idx, P, E,
