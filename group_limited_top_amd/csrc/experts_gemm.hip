@@ -36,6 +36,7 @@
 #include "device.h"
 #include "expert_tiles.h"
 #include "kernels.h"
+#include "ring.h"
 
 namespace moe {
 
@@ -44,13 +45,6 @@ constexpr int kSliceB = 32768;    // bytes of one staged slice
 constexpr int kRingN = 5;         // slice buffers in the ring
 constexpr int kGuFeat = 128;      // h features per gate/up tile
 constexpr int kDnOut = 256;       // output columns per down tile
-
-typedef __attribute__((address_space(3))) const void lvoid_t;
-
-// Scalar (wave-uniform) load through the constant address space.
-__device__ __forceinline__ int32_t sload(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)p;
-}
 
 // One slice's 4 loads of this wave: load j brings the lane's 16 bytes from
 // base + off[j] into LDS lds + 1 KiB j + 16 lane.  M0 (the LDS destination) is
@@ -80,40 +74,6 @@ __device__ __forceinline__ void dma4(const void* base_, const uint32_t (&off)[4]
       : "memory", "scc");
 }
 
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding and its LDS reads are done, then meet the other waves.
-template <int N>
-__device__ __forceinline__ void ring_wait() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Row slices (256 rows x 128 B): 16-byte chunk c of row r sits at
-// r * 128 + 16 (c ^ ((r >> 1) & 7)), so that 16 consecutive rows read at one
-// chunk index cover all 64 banks.  A DMA load j of wave w writes rows
-// 32 w + 8 j + lane / 8, slot lane & 7, i.e. logical chunk rs_chunk(j, lane).
-__device__ __forceinline__ int rs_addr(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
-__device__ __forceinline__ int rs_chunk(int j, int lane) { return (lane & 7) ^ ((4 * j + (lane >> 4)) & 7); }
-
-__device__ __forceinline__ u32x4 lds16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// W_down slices (64 rows k x 512 B): 16-byte chunk c of row r sits at chunk
-// c ^ wd_swz(r).  The transpose reads of one instruction cover 16 rows
-// (8 q + c, q, c = 0..3) at one 32-byte column window; the XOR spreads them
-// over the 8 windows of a 256-byte bank line, two rows each.
-__device__ __forceinline__ int wd_swz(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
-
-// LDS transpose read: within each group of 16 lanes, lane i receives element
-// (i & 3) of the 4 x 16-bit values addressed by lane 4 c + (i >> 2), for
-// c = 0..3.  So if lane 4 c + m of a group points at row c, columns 4 m..4 m + 3
-// of a [k][column] block, lane i gets column i at rows 0..3.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(__attribute__((address_space(3))) uint8_t*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
-
 struct GTile {
   int e, row0, nrows, s;  // expert (E = shared), first row, rows, column slice
 };
@@ -133,33 +93,6 @@ __device__ __forceinline__ GTile gtile(const int32_t* tab, int t, int S) {
   g.s = t - rt * S;
   return g;
 }
-
-// A wave-uniform pointer, made visible as such.
-template <class T>
-__device__ __forceinline__ T* uniform_ptr(T* p) {
-  const uint64_t b = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  return reinterpret_cast<T*>(((uint64_t)hi << 32) | (uint64_t)lo);
-}
-
-// 8-byte store to global memory (a global, not flat, store: flat stores would
-// also count against the LDS counter the ring waits on).  Plain stores: the
-// streaming (nontemporal) kind measured much slower for the down outputs.
-__device__ __forceinline__ void store8(uint16_t* p, u32x2 v) {
-  *(__attribute__((address_space(1))) u32x2*)p = v;
-}
-
-// Vector load of one int32 issued as inline asm: the compiler then inserts no
-// wait for it (which would also wait for the ring's loads).  The caller reads
-// the value only after later ring waits have covered it, and passes it through
-// settle() there so that the read cannot move above them.
-__device__ __forceinline__ int32_t load_i32_async(const int32_t* p) {
-  int32_t v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ void settle(int32_t& v) { asm volatile("" : "+v"(v)); }
 
 // MODE 0: gate/up + SwiGLU; MODE 1: down.
 template <int MODE>
@@ -350,10 +283,15 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
         A[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     }
+    // raised wave priority while issuing the MFMAs, so that the other wave of
+    // the SIMD issues its LDS reads and loads in between rather than racing
+    // this one for the MFMA pipe
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int n = 0; n < 4; ++n) acc[i][n] = mfma16x16x32(A[i], B[n], acc[i][n]);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Every epilogue issues the same number of stores per wave (kStores), rows
   // past the tile's end going to trash (the padding rows of h_routed, whose

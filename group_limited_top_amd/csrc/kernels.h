@@ -78,7 +78,8 @@ int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows);
 // LDS-pipelined MFMA GEMMs (tile_rows == kGRows); shapes with gemm_shape_ok.
 bool gemm_shape_ok(int64_t T, int K, int I, int Is, int H);
 hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
-// gate/up weight streaming through the LDS ring (32-row tiles); usable when stream_ring_ok.
+// gate/up weight streaming through the LDS ring (32-row tiles); usable when
+// stream_ring_ok.
 bool stream_ring_ok(const ExpertArgs& a);
 hipError_t launch_gateup_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,
                                      const StageTimer* tm);
