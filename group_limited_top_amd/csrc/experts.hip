@@ -291,33 +291,41 @@ __global__ __launch_bounds__(256) void k_down_bf16(const ExpertArgs a, int hslic
 // output added as is).
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
+  constexpr int kMaxK = 16;  // top_k <= 16 (the supported envelope)
   const int t = blockIdx.x;
   const int H = a.H, K = a.K;
   const uint16_t* osh = reinterpret_cast<const uint16_t*>(a.o_shared);
   const uint16_t* orr = reinterpret_cast<const uint16_t*>(a.o_routed);
   uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
+  // the token's pair slots and weights, then every row load before any use,
+  // so that the K + 1 loads are in flight together
+  int32_t slot[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;
+    wj[j] = j < K ? a.topk_w[(size_t)t * K + j] : 0.0f;
+  }
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
+    const u32x4 vs = a.Is > 0 ? ld16(osh + (size_t)t * H + c * 8) : zero4;
+    u32x4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) v[j] = slot[j] >= 0 ? ld16(orr + (size_t)slot[j] * H + c * 8) : zero4;
     float acc[8];
-    if (a.Is > 0) {
-      const u32x4 v = ld16(osh + (size_t)t * H + c * 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = bf16_lo(v[i]);
-        acc[2 * i + 1] = bf16_hi(v[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = bf16_lo(vs[i]);
+      acc[2 * i + 1] = bf16_hi(vs[i]);
     }
-    for (int j = 0; j < K; ++j) {
-      const int32_t slot = a.pair_slot[(size_t)t * K + j];
-      if (slot < 0) continue;
-      const float w = a.topk_w[(size_t)t * K + j];
-      const u32x4 v = ld16(orr + (size_t)slot * H + c * 8);
+    // j order, one product and one sum per term, as specified
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (slot[j] < 0) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = acc[2 * i] + w * bf16_lo(v[i]);
-        acc[2 * i + 1] = acc[2 * i + 1] + w * bf16_hi(v[i]);
+        acc[2 * i] = acc[2 * i] + wj[j] * bf16_lo(v[j][i]);
+        acc[2 * i + 1] = acc[2 * i + 1] + wj[j] * bf16_hi(v[j][i]);
       }
     }
     u32x4 pk;
