@@ -86,21 +86,80 @@ class HipEvents:
             self.hip.hipEventDestroy(self.c.c_void_p(h))
 
 
+KERNEL_SOURCES = ("experts.hip", "experts_gemm.hip", "experts_stream.hip", "expert_tiles.h",
+                  "ring.h", "device.h", "kernels.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    csrc = os.path.join(ROOT, "group_limited_top_amd", "csrc")
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                   for f in KERNEL_SOURCES)).hexdigest()
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter runs
     (profiles/traffic.json), or None when the kernel sources changed since."""
-    import hashlib
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[workload][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    csrc = os.path.join(ROOT, "group_limited_top_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                   for f in ("experts.hip", "experts_tiled.hip", "expert_tiles.h", "device.h",
-                             "kernels.h"))
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if kernel_source_hash() != rec["source_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
+
+
+def _counter_means(run_dir, counter):
+    """Per kernel (short name): mean of `counter` per dispatch in a rocprofv3
+    --pmc csv run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    tot, disp = {}, {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("moe::", "").strip()
+            tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+            disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def write_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, note):
+    """profiles/traffic.json entries for every libmoe kernel of `workload`: HBM
+    bytes per launch = FETCH_SIZE x f + WRITE_SIZE x w (KiB), with f and w set
+    so that a plain device copy of copy_mib MiB reads and writes its size."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    cf = _counter_means(copy_fetch_dir, "FETCH_SIZE")
+    cw = _counter_means(copy_write_dir, "WRITE_SIZE")
+    copy_k = [k for k in cf if "copyBuffer" in k]
+    if not copy_k:
+        raise SystemExit("no copy kernel in the calibration runs")
+    kib = copy_mib * 1024.0
+    fscale = round(kib / cf[copy_k[0]], 4)
+    wscale = round(kib / cw[copy_k[0]], 4)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        data = {}
+    entry = {}
+    for k in sorted(fetch):
+        if not k.startswith("k_") or k not in write:
+            continue
+        entry[k] = {"hbm_bytes_per_launch": int(round((fetch[k] * fscale + write[k] * wscale) * 1024)),
+                    "fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                    "fetch_scale": fscale, "write_scale": wscale,
+                    "source_sha256": kernel_source_hash(), "profile": note}
+    data[workload] = entry
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: entry}, indent=1))
 
 
 def cpu_baseline(shape, x, wr, bias, w, max_tokens):
@@ -145,7 +204,16 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
+    ap.add_argument("--write-traffic", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this "
+                         "workload and of --copy-calibration into profiles/traffic.json")
+    ap.add_argument("--profile-note", default="", help="with --write-traffic: the summary file")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic, args.copy_calibration or 1024,
+                      args.profile_note)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this layer's data-parallel share needs no "
               f"exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
