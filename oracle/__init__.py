@@ -11,9 +11,11 @@ weights are passed either as ``np.float32`` arrays or as bf16 bit patterns in
 
 Method source: the page "InternLumina-U2中256个专家的路由秘密：分组受限Top-K、
 Expert Bias与Fused MoE详解", sections 二 (sigmoid router, group-limited top-k,
-weight normalisation), 三 (selection-only expert bias), 四 (stacked SwiGLU
-experts, eager per-expert loop and sort-by-expert inference), 五 (shared
-expert added unweighted), 六 (per-expert hit counts).
+weight normalisation), 三 (selection-only expert bias, and its use for load
+balancing), 四 (stacked SwiGLU experts, eager per-expert loop and
+sort-by-expert inference), 五 (shared expert added unweighted), 六 (per-expert
+hit counts and their statistics); and the page at m.lqnn.cn/news/279712,
+section "MoE 负载均衡 Loss 别忘加" (the auxiliary loss E * sum_i f_i * P_i).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 except the layer output's numeric value at full size, which no page prints
@@ -70,6 +72,10 @@ def _load():
     lib.orc_experts_path_a.argtypes = [P, P, i32, P, P, P, i32, P, i32]
     lib.orc_experts_path_b.argtypes = [P, i32, P, i32, P, P, P, i32]
     lib.orc_rmsnorm.argtypes = [i32, i32, P, i32, ctypes.c_double, P]
+    lib.orc_track.argtypes = [i32, i32, i32, P, P]
+    lib.orc_expert_stats.argtypes = [i32, i32, i32, P, P, P]
+    lib.orc_bias_update.argtypes = [i32, P, P, P, ctypes.c_double]
+    lib.orc_aux_loss.argtypes = [i32, i32, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -285,3 +291,56 @@ def f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     out = (r.view(np.uint32) >> 16).astype(np.uint16)
     out[np.isnan(a)] = 0x7FC0
     return out
+
+
+# --------------------------------------------------------------------------- load balancing
+
+NSTAT = 8
+STAT_NAMES = ("hits", "max_load", "min_load", "cv", "idle", "hottest", "coldest",
+              "max_group_load")
+
+
+def track(idx: np.ndarray, E: int, tracking: np.ndarray | None = None) -> np.ndarray:
+    """tracking[e] += hits of expert e in idx [T, K] (int64 [E], updated in place)."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, K = idx.shape
+    if tracking is None:
+        tracking = np.zeros(E, np.int64)
+    assert tracking.dtype == np.int64 and tracking.flags.c_contiguous and tracking.size == E
+    _load().orc_track(T, K, E, _ptr(idx), _ptr(tracking))
+    return tracking
+
+
+def expert_stats(tracking: np.ndarray, n_group: int):
+    """(load fp32 [L, E], summary fp64 [L, NSTAT]) from tracked hits [L, E]."""
+    tr = np.ascontiguousarray(np.atleast_2d(tracking), dtype=np.int64)
+    L, E = tr.shape
+    load = np.empty((L, E), np.float32)
+    summ = np.empty((L, NSTAT), np.float64)
+    _load().orc_expert_stats(L, E, n_group, _ptr(tr), _ptr(load), _ptr(summ))
+    return load, summ
+
+
+def bias_update(counts: np.ndarray, bias: np.ndarray | None, rate: float) -> np.ndarray:
+    """The expert-bias update from one routing's counts; returns the new bias (fp32)."""
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    E = c.size
+    b = np.zeros(E, np.float32) if bias is None else np.ascontiguousarray(bias, np.float32)
+    out = np.empty(E, np.float32)
+    _load().orc_bias_update(E, _ptr(c), _ptr(b), _ptr(out), float(rate))
+    return out
+
+
+def aux_loss(lam: np.ndarray, counts: np.ndarray):
+    """(f fp64 [E], P fp64 [E], loss float) from fp32 logits [T, E] and counts [E]."""
+    lam = np.ascontiguousarray(lam, dtype=np.float32)
+    T, E = lam.shape
+    if T < 1:
+        raise ValueError("the auxiliary loss needs at least one token")
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    assert c.size == E
+    f = np.empty(E, np.float64)
+    P = np.empty(E, np.float64)
+    loss = np.empty(1, np.float64)
+    _load().orc_aux_loss(T, E, _ptr(lam), _ptr(c), _ptr(f), _ptr(P), _ptr(loss))
+    return f, P, float(loss[0])

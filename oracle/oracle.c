@@ -653,3 +653,129 @@ void orc_rmsnorm(int T, int H, const void* x, int xdt, double eps, double* r) {
     for (int h = 0; h < H; ++h) r[(size_t)t * H + h] = elem(x, xdt, (size_t)t * H + h) * inv;
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Load balancing: hit tracking, its statistics, the expert-bias update and */
+/* the auxiliary loss                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* [Routing §六]: with tracking on, every routing call adds each expert's hits
+ * (a bincount of the chosen indices) to a running per-layer count.  Written
+ * as one pass over the pairs per expert, independently of orc_permute. */
+void orc_track(int T, int K, int E, const int32_t* idx, int64_t* tracking) {
+  int64_t P = (int64_t)T * K;
+  for (int e = 0; e < E; ++e) {
+    int64_t n = 0;
+    for (int64_t p = 0; p < P; ++p)
+      if (idx[p] == e) n += 1;
+    tracking[e] += n;
+  }
+}
+
+/* [Routing §六] / [Pitfalls, MoE 负载均衡 Loss 别忘加]: the load histogram of
+ * each layer's tracked hits h[e], as loads relative to the balanced share
+ * (load[e] = h[e] * E / N, N = sum of h; 1 = balanced) and a summary row:
+ *   0 N, 1 max load, 2 min load, 3 coefficient of variation
+ *   sqrt(mean_e (h[e] - N/E)^2) / (N/E), 4 experts with no hit, 5 the most
+ *   and 6 the least hit expert (lowest index on ties), 7 the largest group
+ *   load, sum of a group's hits * n_group / N.
+ * With N = 0 every ratio is 0, the idle count is E and both indices are 0. */
+void orc_expert_stats(int L, int E, int n_group, const int64_t* tracking, float* load,
+                      double* summary) {
+  int gsize = E / n_group;
+  for (int l = 0; l < L; ++l) {
+    const int64_t* h = tracking + (size_t)l * E;
+    double* s = summary + (size_t)l * ORC_NSTAT;
+    int64_t N = 0, idle = 0;
+    int hot = 0, cold = 0;
+    for (int e = 0; e < E; ++e) {
+      N += h[e];
+      if (h[e] == 0) idle += 1;
+      if (h[e] > h[hot]) hot = e;
+      if (h[e] < h[cold]) cold = e;
+    }
+    int64_t gmax = 0;
+    for (int g = 0; g < n_group; ++g) {
+      int64_t sg = 0;
+      for (int e = g * gsize; e < (g + 1) * gsize; ++e) sg += h[e];
+      if (sg > gmax) gmax = sg;
+    }
+    s[0] = (double)N;
+    s[4] = (double)idle;
+    s[5] = (double)hot;
+    s[6] = (double)cold;
+    if (N == 0) {
+      for (int e = 0; e < E; ++e) load[(size_t)l * E + e] = 0.0f;
+      s[1] = s[2] = s[3] = s[7] = 0.0;
+      continue;
+    }
+    for (int e = 0; e < E; ++e)
+      load[(size_t)l * E + e] = (float)((double)(h[e] * E) / (double)N);
+    s[1] = (double)(h[hot] * E) / (double)N;
+    s[2] = (double)(h[cold] * E) / (double)N;
+    double mean = (double)N / (double)E, ss = 0.0;
+    for (int e = 0; e < E; ++e) {
+      double dv = (double)h[e] - mean;
+      ss += dv * dv;
+    }
+    s[3] = sqrt(ss / (double)E) / mean;
+    s[7] = (double)(gmax * n_group) / (double)N;
+  }
+}
+
+/* [Routing §三]: during training the bias is raised for experts that receive
+ * few tokens and lowered for experts that receive many, steering tokens
+ * toward idle experts; the weights never see it.  The page gives no rule; the
+ * one used here moves each bias against its expert's hit excess, normalised
+ * by the largest excess:
+ *   cbar = sum(counts) / E,  d = max(max_e |counts[e] - cbar|, 1),
+ *   bias_out[e] = RN32(bias_in[e] + (-rate * (counts[e] - cbar)) / d)
+ * in fp64.  From a zero bias with rate 0.1 this is the partly rebalancing
+ * bias of the skewed-routing workload. */
+void orc_bias_update(int E, const int32_t* counts, const float* bias_in, float* bias_out,
+                     double rate) {
+  int64_t N = 0;
+  for (int e = 0; e < E; ++e) N += counts[e];
+  double cbar = (double)N / (double)E;
+  double d = 1.0;
+  for (int e = 0; e < E; ++e) {
+    double ex = fabs((double)counts[e] - cbar);
+    if (ex > d) d = ex;
+  }
+  for (int e = 0; e < E; ++e) {
+    double v = (-rate * ((double)counts[e] - cbar)) / d;
+    bias_out[e] = (float)((double)bias_in[e] + v);
+  }
+}
+
+/* [Pitfalls, MoE 负载均衡 Loss 别忘加]: the classic load-balancing loss
+ * E * sum_i f_i * P_i from the router logits the forward returns.
+ *   f_i = counts[i] / T, the fraction of tokens sent to expert i (the counts
+ *         of the routing actually taken; sum_i f_i = K),
+ *   P_i = (1/T) sum_t softmax(lam[t])_i, the mean router probability.
+ * fp64 throughout (exp from libm); T >= 1. */
+void orc_aux_loss(int T, int E, const float* lam, const int32_t* counts, double* f, double* P,
+                  double* loss) {
+  double* p = (double*)malloc(sizeof(double) * (size_t)E);
+  for (int e = 0; e < E; ++e) P[e] = 0.0;
+  for (int t = 0; t < T; ++t) {
+    const float* l = lam + (size_t)t * E;
+    double m = (double)l[0];
+    for (int e = 1; e < E; ++e)
+      if ((double)l[e] > m) m = (double)l[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp((double)l[e] - m);
+      z += p[e];
+    }
+    for (int e = 0; e < E; ++e) P[e] += p[e] / z;
+  }
+  double acc = 0.0;
+  for (int e = 0; e < E; ++e) {
+    P[e] = P[e] / (double)T;
+    f[e] = (double)counts[e] / (double)T;
+    acc += f[e] * P[e];
+  }
+  *loss = (double)E * acc;
+  free(p);
+}

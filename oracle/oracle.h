@@ -89,6 +89,17 @@ void orc_experts_path_b(const orc_experts_t* ex, int T, const void* x, int xdt,
 /* a9 (layer stack only): r = x / sqrt(mean(x^2) + eps), gamma = 1, fp64. */
 void orc_rmsnorm(int T, int H, const void* x, int xdt, double eps, double* r);
 
+/* Load balancing ([Routing §三, §六], [Pitfalls, MoE 负载均衡 Loss 别忘加]);
+ * definitions in oracle.c. */
+enum { ORC_NSTAT = 8 };
+void orc_track(int T, int K, int E, const int32_t* idx, int64_t* tracking);
+void orc_expert_stats(int L, int E, int n_group, const int64_t* tracking, float* load,
+                      double* summary);
+void orc_bias_update(int E, const int32_t* counts, const float* bias_in, float* bias_out,
+                     double rate);
+void orc_aux_loss(int T, int E, const float* lam, const int32_t* counts, double* f, double* P,
+                  double* loss);
+
 #ifdef __cplusplus
 }
 #endif

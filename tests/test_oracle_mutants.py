@@ -20,6 +20,7 @@ HDR = os.path.join(ROOT, "oracle", "oracle.h")
 R = "tests/test_oracle_routing.py"
 X = "tests/test_oracle_experts.py"
 S = "tests/test_oracle_sigmoid.py"
+B = "tests/test_oracle_balance.py"
 
 MUTANTS = {
     "group_score_top1": ("  return m1 + m2;", "  return m1 + m1;", [R + "::test_brute_force_full_shape"]),
@@ -51,6 +52,22 @@ MUTANTS = {
                         [X + "::test_zero_weights_leave_shared_expert_unweighted"]),
     "sigmoid_bad_coefficient": ("    taylor_c[i] = 1.0 / fact;", "    taylor_c[i] = 1.0 / (fact + (i == 5));",
                                 [S + "::test_accuracy_and_monotonicity_sampled"]),
+    "track_no_accumulate": ("    tracking[e] += n;", "    tracking[e] = n;",
+                            [B + "::test_track_hand_example_and_accumulation"]),
+    "stats_sample_variance": ("s[3] = sqrt(ss / (double)E) / mean;",
+                              "s[3] = sqrt(ss / (double)(E - 1)) / mean;", [B + "::test_stats_hand_example"]),
+    "stats_cold_tie_to_higher": ("if (h[e] < h[cold]) cold = e;", "if (h[e] <= h[cold]) cold = e;",
+                                 [B + "::test_stats_ties_take_the_lowest_index"]),
+    "bias_step_sign": ("double v = (-rate * ((double)counts[e] - cbar)) / d;",
+                       "double v = (rate * ((double)counts[e] - cbar)) / d;",
+                       [B + "::test_bias_update_hand_example"]),
+    "bias_not_normalised": ("    if (ex > d) d = ex;", "    ;", [B + "::test_bias_update_hand_example"]),
+    "aux_no_num_experts": ("  *loss = (double)E * acc;", "  *loss = acc;", [B + "::test_aux_loss_balanced_is_k"]),
+    "aux_unnormalised_probs": ("    for (int e = 0; e < E; ++e) P[e] += p[e] / z;",
+                               "    for (int e = 0; e < E; ++e) P[e] += p[e];",
+                               [B + "::test_aux_loss_balanced_is_k"]),
+    "aux_sigmoid_probs": ("      p[e] = exp((double)l[e] - m);", "      p[e] = 1.0 / (1.0 + exp(-(double)l[e]));",
+                          [B + "::test_aux_loss_closed_form_one_large_logit"]),
     "sigmoid_sign": ("  double t = -(double)z;", "  double t = (double)z;", [S + "::test_textbook_values"]),
 }
 
