@@ -191,6 +191,62 @@ def cpu_baseline(shape, x, wr, bias, w, max_tokens):
             "kind": "oracle", "sample": sample}
 
 
+def bench_balance(L, d, shape, xd, weights, ws, K):
+    """Load-balancing kernels at this workload: the auxiliary loss over the
+    forward's router logits and counts, the expert-bias update, and the
+    load statistics of a 19-layer tracking table (the model's MoE layers).
+    Each is timed over K back-to-back calls with events on the stream the
+    binding launches on; algorithmic bytes are what each call must read and
+    write once."""
+    import torch
+    dev = xd.device
+    T, E = shape.T, shape.E
+    y = torch.empty(T, shape.H, dtype=shape.torch_dtype, device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    d.flags |= L.MOE_F_WRITE_LOGITS
+    L.moe_layer_forward(d, xd, weights, y, logits_out=logits, counts_out=counts, ws=ws)
+    d.flags &= ~L.MOE_F_WRITE_LOGITS
+    aux_ws = L.aux_loss_workspace(T, E, dev)
+    tracking = counts.to(torch.int64).repeat(19, 1).contiguous()
+    load = torch.empty(19, E, dtype=torch.float32, device=dev)
+    summ = torch.empty(19, L.MOE_NSTAT, dtype=torch.float64, device=dev)
+    bias = torch.zeros(E, dtype=torch.float32, device=dev)
+    aux_out = (torch.empty(E, dtype=torch.float64, device=dev),
+               torch.empty(E, dtype=torch.float64, device=dev),
+               torch.empty(1, dtype=torch.float64, device=dev))
+    calls = {
+        "aux_loss": (lambda: L.moe_aux_loss(logits, counts, aux_ws, aux_out),
+                     T * E * 4 + E * 4 + 2 * E * 8 + 8),
+        "bias_update": (lambda: L.moe_bias_update(counts, bias, bias, 1e-3), E * 4 * 3),
+        "expert_stats_19_layers": (lambda: L.moe_expert_stats(tracking, shape.n_group, load, summ),
+                                   19 * E * (8 + 4) + 19 * L.MOE_NSTAT * 8),
+    }
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        # K calls captured in one HIP graph, so that host launch cost does not
+        # space out kernels of a few microseconds
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(K):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / K * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+                     "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +395,7 @@ def main():
                    "ms_per_step_eager_with_kernel_events": round(ms_step, 4),
                    "ms_per_step_eager": round(ms_step_plain, 4)},
     }
+    out["balance"] = bench_balance(L, d, shape, xd, weights, ws, K)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, x, wr, bias, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -24,8 +24,12 @@ MOE_STATUS_NONFINITE, MOE_STATUS_BAD_INDEX = 1, 2
 EXPORTS = (
     "moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_layer_forward",
     "moe_residual_rmsnorm", "moe_status", "moe_sigmoid32", "moe_strerror",
-    "moe_layer_forward_timed", "moe_stage_kernel",
+    "moe_layer_forward_timed", "moe_stage_kernel", "moe_expert_stats", "moe_bias_update",
+    "moe_aux_loss_workspace_size", "moe_aux_loss",
 )
+MOE_NSTAT = 8
+STAT_NAMES = ("hits", "max_load", "min_load", "cv", "idle", "hottest", "coldest",
+              "max_group_load")
 # kernel stages (moe_stage_t), in launch order
 STAGES = ("router_split", "logits", "select", "hist", "scan", "scatter", "tiles", "gate_up",
           "down", "combine")
@@ -82,6 +86,15 @@ def _load():
     lib.moe_sigmoid32.restype = i
     lib.moe_stage_kernel.argtypes = [D, i]
     lib.moe_stage_kernel.restype = ctypes.c_char_p
+    i32 = ctypes.c_int32
+    lib.moe_expert_stats.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.moe_expert_stats.restype = i
+    lib.moe_bias_update.argtypes = [i32, P, P, P, ctypes.c_double, P]
+    lib.moe_bias_update.restype = i
+    lib.moe_aux_loss_workspace_size.argtypes = [i32, i32]
+    lib.moe_aux_loss_workspace_size.restype = S
+    lib.moe_aux_loss.argtypes = [i32, i32, P, P, P, P, P, P, S, P]
+    lib.moe_aux_loss.restype = i
     lib.moe_strerror.argtypes = [i]
     lib.moe_strerror.restype = ctypes.c_char_p
     return lib
@@ -298,6 +311,67 @@ def moe_sigmoid32(z, s, stream=None):
     zp = _check(z, "z", tuple(z.shape), torch.float32, dev)
     sp = _check(s, "s", tuple(z.shape), torch.float32, dev)
     _rc(LIB.moe_sigmoid32(zp, sp, z.numel(), _stream(stream)), "moe_sigmoid32")
+
+
+# ---------------------------------------------------------------------------- load balancing
+
+def moe_expert_stats(tracking, n_group: int, load=None, summary=None, stream=None):
+    """Load statistics of tracked hits [L, E] int64 (one row per layer):
+    returns (load fp32 [L, E], summary fp64 [L, MOE_NSTAT]) (see STAT_NAMES)."""
+    if tracking.dim() == 1:
+        tracking = tracking.view(1, -1)
+    Lr, E = tracking.shape
+    dev = tracking.device
+    if load is None:
+        load = torch.empty(Lr, E, dtype=torch.float32, device=dev)
+    if summary is None:
+        summary = torch.empty(Lr, MOE_NSTAT, dtype=torch.float64, device=dev)
+    tp = _check(tracking, "tracking", (Lr, E), torch.int64, dev)
+    lp = _check(load, "load", (Lr, E), torch.float32, dev)
+    sp = _check(summary, "summary", (Lr, MOE_NSTAT), torch.float64, dev)
+    _rc(LIB.moe_expert_stats(Lr, E, n_group, tp, lp, sp, _stream(stream)), "moe_expert_stats")
+    return load, summary
+
+
+def moe_bias_update(counts, bias_in, bias_out, rate: float, stream=None):
+    """bias_out = bias_in moved against each expert's hit excess (bias_in may
+    be None = zeros, or the same tensor as bias_out)."""
+    E = counts.numel()
+    dev = counts.device
+    cp = _check(counts, "counts", (E,), torch.int32, dev)
+    bi = _check(bias_in, "bias_in", (E,), torch.float32, dev, optional=True)
+    bo = _check(bias_out, "bias_out", (E,), torch.float32, dev)
+    _rc(LIB.moe_bias_update(E, cp, bi, bo, float(rate), _stream(stream)), "moe_bias_update")
+
+
+def aux_loss_workspace(T: int, E: int, device="cuda") -> torch.Tensor:
+    n = LIB.moe_aux_loss_workspace_size(T, E)
+    if n == 0:
+        raise MoeError(-1, "moe_aux_loss_workspace_size (invalid sizes)")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_aux_loss(logits, counts, ws=None, out=None, stream=None):
+    """(f fp64 [E], P fp64 [E], loss fp64 [1]) of the load-balancing loss
+    E * sum_i f_i * P_i from router logits [T, E] fp32 and counts [E] int32;
+    `out` may supply the three result tensors."""
+    T, E = logits.shape
+    dev = logits.device
+    if ws is None:
+        ws = aux_loss_workspace(T, E, dev)
+    if out is None:
+        out = (torch.empty(E, dtype=torch.float64, device=dev),
+               torch.empty(E, dtype=torch.float64, device=dev),
+               torch.empty(1, dtype=torch.float64, device=dev))
+    f, P, loss = out
+    lp = _check(logits, "logits", (T, E), torch.float32, dev)
+    cp = _check(counts, "counts", (E,), torch.int32, dev)
+    fp = _check(f, "f", (E,), torch.float64, dev)
+    pp = _check(P, "P", (E,), torch.float64, dev)
+    sp = _check(loss, "loss", (1,), torch.float64, dev)
+    wp, wn = _ws(None, ws)
+    _rc(LIB.moe_aux_loss(T, E, lp, cp, fp, pp, sp, wp, wn, _stream(stream)), "moe_aux_loss")
+    return f, P, loss
 
 
 def moe_stack_forward(d: MoeDesc, x, layers, ws, eps: float = 1e-6, tracking=None,

@@ -360,6 +360,41 @@ int moe_sigmoid32(const float* z, float* s, int64_t n, hipStream_t stream) {
   return hip_rc(moe::launch_sigmoid32(z, s, n, stream));
 }
 
+size_t moe_aux_loss_workspace_size(int32_t T, int32_t E) {
+  if (T < 1 || E < 2 || E > 1024) return 0;
+  return align_up(moe::aux_workspace_bytes(T, E));
+}
+
+int moe_expert_stats(int32_t L, int32_t E, int32_t n_group, const int64_t* tracking, float* load,
+                     double* summary, hipStream_t stream) {
+  if (L < 0 || E < 1 || n_group < 1 || E % n_group != 0) return MOE_ERR_INVALID;
+  if (E > 1024 || n_group > 64) return MOE_ERR_UNSUPPORTED;
+  if (L == 0) return MOE_OK;
+  if (!tracking || !load || !summary) return MOE_ERR_INVALID;
+  if (misaligned(tracking) || misaligned(load) || misaligned(summary)) return MOE_ERR_ALIGN;
+  return hip_rc(moe::launch_expert_stats(tracking, load, summary, L, E, n_group, stream));
+}
+
+int moe_bias_update(int32_t E, const int32_t* counts, const float* bias_in, float* bias_out,
+                    double rate, hipStream_t stream) {
+  if (E < 1 || !counts || !bias_out || !isfinite(rate)) return MOE_ERR_INVALID;
+  if (E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (misaligned(counts) || misaligned(bias_in) || misaligned(bias_out)) return MOE_ERR_ALIGN;
+  return hip_rc(moe::launch_bias_update(counts, bias_in, bias_out, E, rate, stream));
+}
+
+int moe_aux_loss(int32_t T, int32_t E, const float* logits, const int32_t* counts, double* f,
+                 double* P, double* loss, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 1 || E < 2 || !logits || !counts || !f || !P || !loss) return MOE_ERR_INVALID;
+  if (E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < moe_aux_loss_workspace_size(T, E)) return MOE_ERR_WORKSPACE;
+  const void* ps[] = {logits, counts, f, P, loss, ws};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  return hip_rc(moe::launch_aux_loss(logits, counts, f, P, loss, static_cast<double*>(ws), T, E,
+                                     stream));
+}
+
 const char* moe_strerror(int code) {
   switch (code) {
     case MOE_OK: return "success";

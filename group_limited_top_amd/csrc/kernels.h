@@ -90,6 +90,16 @@ hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTim
 // this shape; nullptr for other stages.
 const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int Is, int H, bool bf16);
 
+// Load balancing --------------------------------------------------------------
+constexpr int kNStat = 8;  // summary values per layer (moe_expert_stats)
+hipError_t launch_expert_stats(const int64_t* tracking, float* load, double* summary, int L, int E,
+                               int n_group, hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, const float* bias_in, float* bias_out, int E,
+                              double rate, hipStream_t s);
+size_t aux_workspace_bytes(int T, int E);
+hipError_t launch_aux_loss(const float* logits, const int32_t* counts, double* f, double* P,
+                           double* loss, double* part, int T, int E, hipStream_t s);
+
 // Residual + RMSNorm ----------------------------------------------------------
 hipError_t launch_residual_rmsnorm(bool bf16, const void* x_in, const void* y, void* x_out,
                                    void* r_out, int T, int H, float eps, hipStream_t s);

@@ -208,6 +208,67 @@ int moe_status(void* ws, size_t ws_bytes, hipStream_t stream, uint32_t* status);
  * z (device) [n] fp32 -> s (device) [n] fp32.  For verification. */
 int moe_sigmoid32(const float* z, float* s, int64_t n, hipStream_t stream);
 
+/* ---- load balancing -------------------------------------------------------
+ * [Routing §六] keeps, per layer, a running count of each expert's hits (the
+ * `tracking` that moe_permute / moe_layer_forward accumulate) and reads load
+ * statistics from it; [Routing §三] moves the expert bias against each
+ * expert's load during training (raised for experts that get few tokens,
+ * lowered for those that get many); [Pitfalls, MoE 负载均衡 Loss 别忘加] adds
+ * the load-balancing loss E * sum_i f_i * P_i.  These calls are small
+ * reductions; they follow the conventions above (asynchronous, deterministic,
+ * errors on the host before any launch, 16-byte aligned device pointers). */
+
+#define MOE_NSTAT 8 /* summary values per layer of moe_expert_stats */
+
+/* Load statistics of tracked hits, one row per layer.
+ *   tracking (device) [L][E] int64 hits h[e] >= 0 (h[e] * E must fit int64)
+ *   load     (device) [L][E] fp32: RN32(h[e] * E / N), N = sum_e h[e]; 1 is the
+ *            balanced share; all 0 when N = 0
+ *   summary  (device) [L][MOE_NSTAT] fp64: 0 N; 1 largest load; 2 smallest
+ *            load; 3 coefficient of variation sqrt(mean_e (h[e] - N/E)^2) /
+ *            (N/E); 4 experts with no hit; 5 most and 6 least hit expert
+ *            (lower index on ties); 7 largest group load, (hits of the group,
+ *            experts cut in index order into n_group groups) * n_group / N.
+ *            With N = 0: entries 1, 2, 3, 7 are 0, 4 is E, 5 and 6 are 0.
+ * Every value except entry 3 is exact as defined (one IEEE fp64 rounding per
+ * operation shown); entry 3's sum runs in a fixed order of its own.
+ * L = 0 is a no-op.  MOE_ERR_INVALID: L < 0, E < 1, E % n_group != 0, a null
+ * pointer; MOE_ERR_UNSUPPORTED: E > 1024 or n_group > 64. */
+int moe_expert_stats(int32_t L, int32_t E, int32_t n_group, const int64_t* tracking, float* load,
+                     double* summary, hipStream_t stream);
+
+/* Expert-bias update from one routing's hit counts ([Routing §三]; the page
+ * gives no rule, this one moves each bias against its expert's hit excess
+ * normalised by the largest excess).  In IEEE fp64:
+ *   cbar = sum_e counts[e] / E,  d = max(max_e |counts[e] - cbar|, 1),
+ *   bias_out[e] = RN32(bias_in[e] + (-rate * (counts[e] - cbar)) / d)
+ *   counts   (device) [E] int32, e.g. moe_layer_forward's counts_out
+ *   bias_in  (device) [E] fp32 or NULL (= zeros); bias_out (device) [E] fp32,
+ *            may equal bias_in (update in place)
+ * Results are bit-exact to the formula.  MOE_ERR_INVALID: E < 1, a null
+ * required pointer, non-finite rate; MOE_ERR_UNSUPPORTED: E > 1024. */
+int moe_bias_update(int32_t E, const int32_t* counts, const float* bias_in, float* bias_out,
+                    double rate, hipStream_t stream);
+
+/* Bytes of device workspace moe_aux_loss needs for T tokens and E experts
+ * (0 if T < 1, E < 2 or E > 1024).  Host only. */
+size_t moe_aux_loss_workspace_size(int32_t T, int32_t E);
+
+/* Auxiliary load-balancing loss ([Pitfalls, MoE 负载均衡 Loss 别忘加]) from the
+ * router logits the forward returns (MOE_F_WRITE_LOGITS) and the counts of
+ * the routing taken, all in fp64:
+ *   f[i] = counts[i] / T,  P[i] = (1/T) sum_t softmax(logits[t])[i],
+ *   loss = E * sum_i f[i] * P[i]
+ *   logits (device) [T][E] fp32; counts (device) [E] int32
+ *   f, P   (device) [E] fp64; loss (device) [1] fp64
+ *   ws     (device) moe_aux_loss_workspace_size(T, E) bytes of scratch
+ * f is exact; P and loss carry fp64 rounding of the exponentials and of sums
+ * taken in a fixed order (bit-reproducible).  A non-finite logit makes the
+ * results non-finite.  MOE_ERR_INVALID: T < 1, E < 2, a null pointer;
+ * MOE_ERR_UNSUPPORTED: E > 1024; MOE_ERR_WORKSPACE: ws too small. */
+int moe_aux_loss(int32_t T, int32_t E, const float* logits, const int32_t* counts, double* f,
+                 double* P, double* loss, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of an error code. */
 const char* moe_strerror(int code);
 

@@ -144,3 +144,34 @@ def test_binding_checks_shapes(L):
     with pytest.raises(ValueError):
         L.moe_route(d, x, torch.zeros(256, 2048), None, None, torch.zeros(4, 8, dtype=torch.int32),
                     torch.zeros(4, 8), torch.zeros(16, dtype=torch.uint8))
+
+
+def test_balance_entry_points_reject_bad_arguments(L):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: errors come first
+    odd = ctypes.c_void_p(0x100008)
+    lib = L.LIB
+    # statistics: shapes, nulls, alignment; L = 0 is a no-op
+    assert lib.moe_expert_stats(-1, 256, 8, fake, fake, fake, None) == -1
+    assert lib.moe_expert_stats(1, 255, 8, fake, fake, fake, None) == -1
+    assert lib.moe_expert_stats(1, 2048, 8, fake, fake, fake, None) == -2
+    assert lib.moe_expert_stats(1, 256, 128, fake, fake, fake, None) == -2
+    assert lib.moe_expert_stats(1, 256, 8, None, fake, fake, None) == -1
+    assert lib.moe_expert_stats(1, 256, 8, fake, odd, fake, None) == -4
+    assert lib.moe_expert_stats(0, 256, 8, None, None, None, None) == 0
+    # bias update
+    assert lib.moe_bias_update(0, fake, None, fake, 0.1, None) == -1
+    assert lib.moe_bias_update(256, None, None, fake, 0.1, None) == -1
+    assert lib.moe_bias_update(256, fake, None, fake, float("inf"), None) == -1
+    assert lib.moe_bias_update(4096, fake, None, fake, 0.1, None) == -2
+    assert lib.moe_bias_update(256, fake, odd, fake, 0.1, None) == -4
+    # aux loss: the mean over tokens needs one; workspace sized by T and E
+    assert lib.moe_aux_loss_workspace_size(0, 256) == 0
+    assert lib.moe_aux_loss_workspace_size(16, 2048) == 0
+    n = lib.moe_aux_loss_workspace_size(16384, 256)
+    assert n >= 256 * 8 and n % 256 == 0
+    assert lib.moe_aux_loss(0, 256, fake, fake, fake, fake, fake, fake, n, None) == -1
+    assert lib.moe_aux_loss(16384, 256, None, fake, fake, fake, fake, fake, n, None) == -1
+    assert lib.moe_aux_loss(16384, 2048, fake, fake, fake, fake, fake, fake, n, None) == -2
+    assert lib.moe_aux_loss(16384, 256, fake, fake, fake, fake, fake, fake, n - 1, None) == -3
+    assert lib.moe_aux_loss(16384, 256, fake, fake, fake, fake, fake, None, n, None) == -3
+    assert lib.moe_aux_loss(16384, 256, fake, fake, odd, fake, fake, fake, n, None) == -4

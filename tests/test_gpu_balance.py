@@ -1,0 +1,217 @@
+"""GPU parity of the load-balancing kernels (called through the C ABI) against
+the oracle: statistics of tracked hits ([Routing §六]), the expert-bias update
+([Routing §三]) and the auxiliary loss ([Pitfalls, MoE 负载均衡 Loss 别忘加]).
+
+Bars: everything the header calls exact is compared bit for bit (loads,
+counts-derived summary entries, the bias update, f); the coefficient of
+variation, P and the loss carry fp64 sums in another order and exponentials
+from another library: relative 1e-12.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_limited_top_amd import synth
+
+from gpu_helpers import DEV, L, gpu_layer, make_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+# --------------------------------------------------------------------------- statistics
+
+def _tracking_cases(E, rng):
+    rows = [
+        rng.integers(0, 5000, E),                                   # noisy
+        np.zeros(E, np.int64),                                      # nothing tracked
+        np.where(np.arange(E) == E // 3, 123456, 0),                # one expert takes all
+        np.full(E, 7),                                              # balanced
+        (1e6 * (np.arange(1, E + 1) ** -1.2)).astype(np.int64),     # Zipf
+        rng.integers(0, 2 ** 40, E),                                # long-running counts
+        np.repeat(rng.integers(0, 3, E // 2 + 1), 2)[:E],           # ties everywhere
+    ]
+    return np.stack(rows).astype(np.int64)
+
+
+@pytest.mark.parametrize("E,G", [(256, 8), (64, 4), (1000, 8), (1024, 64), (3, 1)])
+def test_expert_stats_match_oracle(E, G):
+    say("expert stats", E, G)
+    rng = np.random.default_rng(E + G)
+    tr = _tracking_cases(E, rng)
+    load, summ = L().moe_expert_stats(torch.from_numpy(tr).to(DEV), G)
+    torch.cuda.synchronize()
+    rl, rs = oracle.expert_stats(tr, G)
+    np.testing.assert_array_equal(load.cpu().numpy().view(np.uint32), rl.view(np.uint32))
+    got = summ.cpu().numpy()
+    exact = [0, 1, 2, 4, 5, 6, 7]
+    np.testing.assert_array_equal(got[:, exact], rs[:, exact])
+    np.testing.assert_allclose(got[:, 3], rs[:, 3], rtol=1e-12, atol=0)
+
+
+def test_expert_stats_of_a_tracked_stack():
+    """Tracking accumulated by the forward over two calls, one row per layer."""
+    say("expert stats of tracked layers")
+    shape = synth.small_shape(300, H=256, I=64, I_shared=64, seed=31)
+    d = L().desc_from_shape(shape)
+    tracking = torch.zeros(3, shape.E, dtype=torch.int64, device=DEV)
+    idx_all = []
+    for layer in range(3):
+        dev = make_layer(shape, layer=layer)
+        for _ in range(2):
+            out = gpu_layer(d, dev, logits=False, tracking=tracking[layer])
+        idx_all.append(out["idx"].cpu().numpy())
+    load, summ = L().moe_expert_stats(tracking, shape.n_group)
+    torch.cuda.synchronize()
+    tr = tracking.cpu().numpy()
+    for layer in range(3):
+        np.testing.assert_array_equal(tr[layer], 2 * oracle.track(idx_all[layer], shape.E))
+    rl, rs = oracle.expert_stats(tr, shape.n_group)
+    np.testing.assert_array_equal(load.cpu().numpy(), rl)
+    np.testing.assert_allclose(summ.cpu().numpy(), rs, rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------- bias update
+
+@pytest.mark.parametrize("E", [256, 64, 1000, 1])
+@pytest.mark.parametrize("rate", [0.1, 1e-3])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_bias_update_bit_exact(E, rate, with_bias):
+    say("bias update", E, rate, with_bias)
+    rng = np.random.default_rng(E)
+    cases = [rng.integers(0, 5000, E), np.full(E, 9), np.zeros(E),
+             np.where(np.arange(E) < 3, 100000, 1)]
+    for c in cases:
+        c = c.astype(np.int32)
+        b0 = (rng.standard_normal(E) * 0.05).astype(np.float32) if with_bias else None
+        ct = torch.from_numpy(c).to(DEV)
+        bi = None if b0 is None else torch.from_numpy(b0).to(DEV)
+        bo = torch.empty(E, dtype=torch.float32, device=DEV)
+        L().moe_bias_update(ct, bi, bo, rate)
+        torch.cuda.synchronize()
+        want = oracle.bias_update(c, b0, rate)
+        np.testing.assert_array_equal(bo.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        if bi is not None:  # in place gives the same bits
+            L().moe_bias_update(ct, bi, bi, rate)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(bi.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_bias_update_from_skewed_routing_counts():
+    """The skewed workload's bias rule on the GPU, from the GPU's own first
+    routing pass: bit-exact against the oracle given the same counts."""
+    say("bias update from skewed routing counts")
+    shape = synth.WORKLOADS["skew_t64k"]
+    d = L().desc_from_shape(shape)
+    x, wr, _ = synth.router_inputs(shape)
+    idx = torch.empty(shape.T, shape.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(shape.T, shape.top_k, dtype=torch.float32, device=DEV)
+    ws = L().alloc_workspace(d, DEV)
+    L().moe_route(d, x.to(DEV), wr.to(DEV), None, None, idx, w, ws)
+    P = shape.T * shape.top_k
+    counts = torch.empty(shape.E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(shape.E + 1, dtype=torch.int32, device=DEV)
+    sp = torch.empty(P, dtype=torch.int32, device=DEV)
+    ps = torch.empty(P, dtype=torch.int32, device=DEV)
+    L().moe_permute(d, idx, counts, offsets, sp, ps, None, ws)
+    bias = torch.empty(shape.E, dtype=torch.float32, device=DEV)
+    L().moe_bias_update(counts, None, bias, 0.1)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    np.testing.assert_array_equal(c, np.bincount(idx.cpu().numpy().ravel(), minlength=shape.E))
+    want = oracle.bias_update(c, None, 0.1)
+    np.testing.assert_array_equal(bias.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    # and it is the workload's own recipe
+    np.testing.assert_array_equal(want, synth.skew_bias_from_counts(c, shape.T, 8).numpy())
+
+
+def test_balancing_loop_bit_exact():
+    """Route, count, update the bias, route again: five rounds entirely on the
+    GPU (exact logits through one-hot x rows), against the same loop in the
+    oracle, compared bit for bit after every round."""
+    say("balancing loop")
+    T, E = 1024, 256
+    rng = np.random.default_rng(77)
+    lam = (rng.standard_normal((T, E)) + synth.skew_offsets(E, 8, 7).numpy()).astype(np.float32)
+    H = T
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    x[torch.arange(T), torch.arange(T)] = 1.0
+    wr = torch.from_numpy(lam.T.copy()).contiguous()
+    d = L().make_desc(T, H, E=E, I=64, I_shared=0)
+    ws = L().alloc_workspace(d, DEV)
+    xt, wrt = x.to(DEV), wr.to(DEV)
+    bias = torch.zeros(E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, 8, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, 8, dtype=torch.float32, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    sp = torch.empty(T * 8, dtype=torch.int32, device=DEV)
+    ps = torch.empty(T * 8, dtype=torch.int32, device=DEV)
+    tracking = torch.zeros(E, dtype=torch.int64, device=DEV)
+    b_ref = np.zeros(E, np.float32)
+    tr_ref = np.zeros(E, np.int64)
+    for it in range(5):
+        L().moe_route(d, xt, wrt, bias, None, idx, w, ws)
+        L().moe_permute(d, idx, counts, offsets, sp, ps, tracking, ws)
+        L().moe_bias_update(counts, bias, bias, 0.01)
+        torch.cuda.synchronize()
+        ri, rw, _ = oracle.select(lam, b_ref, 8, 4, 8, 2.5)
+        rc = np.bincount(ri.ravel(), minlength=E).astype(np.int32)
+        oracle.track(ri, E, tr_ref)
+        b_ref = oracle.bias_update(rc, b_ref, 0.01)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+        np.testing.assert_array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32))
+        np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+        np.testing.assert_array_equal(bias.cpu().numpy().view(np.uint32), b_ref.view(np.uint32))
+    np.testing.assert_array_equal(tracking.cpu().numpy(), tr_ref)
+    _, s = L().moe_expert_stats(tracking, 8)
+    _, rs = oracle.expert_stats(tr_ref, 8)
+    np.testing.assert_allclose(s.cpu().numpy(), rs, rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------- auxiliary loss
+
+def _check_aux(lam, counts):
+    f, P, loss = L().moe_aux_loss(torch.from_numpy(lam).to(DEV), torch.from_numpy(counts).to(DEV))
+    torch.cuda.synchronize()
+    rf, rP, rloss = oracle.aux_loss(lam, counts)
+    np.testing.assert_array_equal(f.cpu().numpy(), rf)
+    np.testing.assert_allclose(P.cpu().numpy(), rP, rtol=1e-12, atol=0)
+    assert abs(float(loss.item()) - rloss) <= 1e-12 * abs(rloss)
+    return float(loss.item())
+
+
+@pytest.mark.parametrize("T,E", [(1, 256), (37, 64), (300, 256), (513, 1000), (2048, 1024),
+                                 (5, 2)])
+def test_aux_loss_small(T, E):
+    say("aux loss", T, E)
+    rng = np.random.default_rng(T + E)
+    lam = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    counts = rng.integers(0, 3 * T, E).astype(np.int32)
+    _check_aux(lam, counts)
+
+
+def test_aux_loss_closed_forms():
+    say("aux loss closed forms")
+    # equal logits and balanced counts: loss = top_k exactly
+    T, E = 64, 256
+    loss = _check_aux(np.zeros((T, E), np.float32), np.full(E, T * 8 // E, np.int32))
+    assert loss == 8.0
+
+
+def test_aux_loss_of_the_forward_logits():
+    """The aux loss from the router logits and counts moe_layer_forward
+    returns at full size (16384 tokens, with expert bias)."""
+    say("aux loss of full_t16k_bias forward")
+    shape = synth.WORKLOADS["full_t16k_bias"]
+    d = L().desc_from_shape(shape)
+    dev = make_layer(shape)
+    out = gpu_layer(d, dev, logits=True)
+    lam = out["logits"].cpu().numpy()
+    c = out["counts"].cpu().numpy()
+    assert c.sum() == shape.T * shape.top_k
+    _check_aux(lam, c)
