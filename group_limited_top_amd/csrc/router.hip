@@ -101,15 +101,18 @@ hipError_t launch_split_router(const float* w, uint16_t* split, int E, int H, hi
 // w = hi + mid + lo (three bf16 parts), fp32 accumulation.  [Routing §二 step
 // 1]: a linear layer in fp32 with no bias term.
 //
-// Block: 4 waves, tile 64 tokens (16 per wave) x 64 experts (4 MFMA N-tiles),
-// K range [z*KR, (z+1)*KR) with z = blockIdx.z (a K split for small T; the
-// partial sums are added in fixed order by the selection kernel).  The weight
-// tile of each 64-deep K chunk is staged in LDS as three bf16 planes, split
-// from fp32 inside the kernel (SPLIT, small T: each element is split by at
-// most a few blocks) or copied from the pre-split planes (large T).  x rows go
-// straight from global memory into the A operands.
+// Block: 4 waves, tile 64 MT tokens (16 MT per wave, MT MFMA M-tiles) x 64
+// experts (4 MFMA N-tiles), K range [z*KR, (z+1)*KR) with z = blockIdx.z (a K
+// split; the partial sums are added in fixed order by the selection kernel).
+// The weight tile of each 64-deep K chunk is staged in LDS as three bf16
+// planes, split from fp32 inside the kernel (SPLIT, small T: each element is
+// split by at most a few blocks) or copied from the pre-split planes (large
+// T).  x rows go straight from global memory into the A operands.  Each
+// staged weight operand feeds MT x 3 MFMAs, so large T uses MT = 4 (the LDS
+// reads per MFMA are a quarter of MT = 1's).
 // ----------------------------------------------------------------------------
-constexpr int kLgBM = 64, kLgBN = 64, kLgKC = 64, kLgRow = kLgKC;
+constexpr int kLgBN = 64, kLgKC = 64, kLgRow = kLgKC;
+constexpr int kLgMTSmall = 1, kLgMTLarge = 4;  // SPLIT (small T) / pre-split (large T)
 
 // LDS element offset of 16-byte chunk c (8 bf16) of staged weight row r: the
 // chunk index is XORed with bits 1..3 of the row, so that 16 consecutive rows
@@ -125,24 +128,27 @@ __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
-template <bool SPLIT>
+template <bool SPLIT, int MT>
 __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict__ x,
                                                       const float* __restrict__ w32,
                                                       const uint16_t* __restrict__ wsplit,
                                                       float* __restrict__ out, int T, int H,
                                                       int E, int KR) {
-  __shared__ uint16_t wl[2][3][kLgBN][kLgRow];  // 55 KB
+  __shared__ uint16_t wl[2][3][kLgBN][kLgRow];  // 48 KiB
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int t0 = blockIdx.x * kLgBM, e0 = blockIdx.y * kLgBN, kbeg = blockIdx.z * KR;
+  const int t0 = blockIdx.x * (64 * MT) + wave * (16 * MT), e0 = blockIdx.y * kLgBN;
+  const int kbeg = blockIdx.z * KR;
   // staging role: expert row er, 16 consecutive k at ks16
   const int er = threadIdx.x >> 2, ks16 = (threadIdx.x & 3) * 16;
   const int erc = min(e0 + er, E - 1);
   const float* wsrc32 = SPLIT ? w32 + (size_t)erc * H + kbeg + ks16 : nullptr;
   const uint16_t* wsrc16 = SPLIT ? nullptr : wsplit + (size_t)erc * H + kbeg + ks16;
   const size_t plane = (size_t)E * H;
-  const int ta = min(t0 + wave * 16 + r, T - 1);
-  const uint16_t* xa = x + (size_t)ta * H + kbeg + q * 8;
+  const uint16_t* xa[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    xa[m] = x + (size_t)min(t0 + 16 * m + r, T - 1) * H + kbeg + q * 8;
 
   u32x4 st[6];  // staged global data: 16 fp32 (SPLIT) or 3 x 16 bf16
   auto load_w = [&](int c) {
@@ -182,14 +188,18 @@ __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict_
     }
   };
 
-  f32x4 acc[4];
+  f32x4 acc[MT][4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nchunks = KR / kLgKC;
-  u32x4 a_cur[2], a_nxt[2];
+  u32x4 a_cur[MT][2], a_nxt[MT][2];
   load_w(0);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) a_cur[s] = ld16(xa + s * 32);
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) a_cur[m][s] = ld16(xa[m] + s * 32);
   store_w(0);
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
@@ -198,7 +208,9 @@ __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict_
     if (more) {
       load_w(c + 1);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) a_nxt[s] = ld16(xa + (c + 1) * kLgKC + s * 32);
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) a_nxt[m][s] = ld16(xa[m] + (c + 1) * kLgKC + s * 32);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -208,52 +220,63 @@ __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict_
         for (int p = 0; p < 3; ++p) {
           const u32x4 b =
               *reinterpret_cast<const u32x4*>(&wl[buf][p][0][0] + lg_swz(n * 16 + r, s * 4 + q));
-          acc[n] = mfma16x16x32(a_cur[s], b, acc[n]);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[m][n] = mfma16x16x32(a_cur[m][s], b, acc[m][n]);
         }
       }
     }
     if (more) {
       store_w(buf ^ 1);
-      a_cur[0] = a_nxt[0];
-      a_cur[1] = a_nxt[1];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        a_cur[m][0] = a_nxt[m][0];
+        a_cur[m][1] = a_nxt[m][1];
+      }
     }
     __syncthreads();
   }
-  // lane holds C[token 4q + i][expert r] of N-tile n
+  // lane holds C[token 4q + i][expert r] of M-tile m, N-tile n
   float* o = out + (size_t)blockIdx.z * T * E;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int e = e0 + n * 16 + r;
     if (e < E) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wave * 16 + 4 * q + i;
-        if (t < T) o[(size_t)t * E + e] = acc[n][i];
-      }
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * m + 4 * q + i;
+          if (t < T) o[(size_t)t * E + e] = acc[m][n][i];
+        }
     }
   }
 }
 
+bool logits_split_in_kernel(int T) { return T <= 1024; }
+
+static int logits_bm(int T) { return 64 * (logits_split_in_kernel(T) ? kLgMTSmall : kLgMTLarge); }
+
 int logits_ksplit(int T, int H, int E) {
-  const int tiles = ((T + kLgBM - 1) / kLgBM) * ((E + kLgBN - 1) / kLgBN);
+  const int bm = logits_bm(T);
+  const int tiles = ((T + bm - 1) / bm) * ((E + kLgBN - 1) / kLgBN);
   int ks = 1;
   while (ks < kMaxKSplit && tiles * ks * 2 <= 512 && (H / kLgKC) % (ks * 2) == 0) ks *= 2;
   return ks;
 }
 
-bool logits_split_in_kernel(int T) { return T <= 1024; }
-
 hipError_t launch_logits_bf16(const uint16_t* x, const float* w32, const uint16_t* wsplit,
                               float* out, int T, int H, int E, int ks, hipStream_t s,
                               const StageTimer* tm) {
-  dim3 grid((unsigned)((T + kLgBM - 1) / kLgBM), (unsigned)((E + kLgBN - 1) / kLgBN), (unsigned)ks);
+  const int bm = logits_bm(T);
+  dim3 grid((unsigned)((T + bm - 1) / bm), (unsigned)((E + kLgBN - 1) / kLgBN), (unsigned)ks);
   const int KR = H / ks;
   stage_begin(tm, kLogits, s);
   if (logits_split_in_kernel(T))
-    hipLaunchKernelGGL(k_logits_bf16<true>, grid, dim3(256), 0, s, x, w32, wsplit, out, T, H, E, KR);
+    hipLaunchKernelGGL((k_logits_bf16<true, kLgMTSmall>), grid, dim3(256), 0, s, x, w32, wsplit,
+                       out, T, H, E, KR);
   else
-    hipLaunchKernelGGL(k_logits_bf16<false>, grid, dim3(256), 0, s, x, w32, wsplit, out, T, H, E,
-                       KR);
+    hipLaunchKernelGGL((k_logits_bf16<false, kLgMTLarge>), grid, dim3(256), 0, s, x, w32, wsplit,
+                       out, T, H, E, KR);
   stage_end(tm, kLogits, s);
   return hipGetLastError();
 }

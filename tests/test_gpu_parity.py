@@ -204,6 +204,26 @@ def test_route_random_full_size(name):
     assert stats["decided"] >= 0.9 * T
 
 
+@pytest.mark.parametrize("T", [1025, 2999])
+def test_route_random_ragged_large(T):
+    """Token counts past the small-batch router path that end in a partial
+    token tile (the large-batch logits kernel covers 256 tokens per block)."""
+    shape = synth.small_shape(T, H=2048, I=64, I_shared=0, bias="normal", seed=900 + T)
+    say("route random ragged", T)
+    x, wr, b = synth.router_inputs(shape)
+    d = L().desc_from_shape(shape, flags=L().MOE_F_WRITE_LOGITS)
+    E = shape.E
+    idx = torch.empty(T, 8, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, 8, dtype=torch.float32, device=DEV)
+    lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    ws = L().alloc_workspace(d, DEV)
+    L().moe_route(d, x.to(DEV), wr.to(DEV), b.to(DEV), lg, idx, w, ws)
+    torch.cuda.synchronize()
+    l64 = oracle.logits(nb(x), wr.numpy())
+    stats = check_routing_random(d, {"expert_bias": b}, {"logits": lg, "idx": idx, "w": w}, l64)
+    assert stats["decided"] >= 0.9 * T
+
+
 # --------------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,kind", [(1, "uniform"), (77, "uniform"), (512, "uniform"),
