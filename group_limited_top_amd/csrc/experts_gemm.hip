@@ -97,7 +97,7 @@ __device__ __forceinline__ GTile gtile(const int32_t* tab, int t, int S) {
 // MODE 0: gate/up + SwiGLU; MODE 1: down.
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int S) {
-  constexpr int kStores = MODE == 0 ? 16 : 32;  // epilogue stores per wave
+  constexpr int kStores = 16;  // epilogue stores per wave (8 bytes each for gate/up, 16 for down)
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingN * kSliceB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,29 +176,34 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
     // whole tile, so rows past the tile's end are readable)
     xo[j] = (uint32_t)((32 * w + 8 * j + (lane >> 3)) * I * 2 + rs_chunk(j, lane) * 16);
   }
+  // The sorted pairs of a tile's rows 32 w + 8 j + lane / 8 (rows past the
+  // tile's end repeat its last row), read with scalar loads: they wait on
+  // lgkmcnt, never on the ring's vmcnt, and arrive in registers the compiler
+  // knows about.  Each lane then picks its row's value.
   auto fetch_rows = [&](int t) __attribute__((always_inline)) {
     const GTile g = gtile(tab_p, t, S);
     pe = g.e;
     prow0 = g.row0;
     if (MODE == 0 && g.e < E) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ptok[j] = load_i32_async(sp_p + g.row0 +
-                                 min(32 * w + 8 * j + (lane >> 3), g.nrows - 1));
+      for (int j = 0; j < 4; ++j) {
+        int32_t v = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int32_t sv = sload(sp_p + g.row0 + min(32 * w + 8 * j + k, g.nrows - 1));
+          v = (lane >> 3) == k ? sv : v;
+        }
+        ptok[j] = v;
+      }
     }
   };
   fetch_rows(first);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first tile's rows, before any ring load
   auto issue_x = [&](uint32_t lds) __attribute__((always_inline)) {
     if (xk == 0) {
       ++xm;
       if (MODE == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // ptok was loaded a whole tile (H / 64 >= 4 steps) ago: the ring
-          // waits since then, each leaving at most 4 + kStores loads
-          // outstanding while at least 8 were issued per step, have covered it
-          settle(ptok[j]);
           const int tok = pe < E ? ptok[j] / K : prow0 + 32 * w + 8 * j + (lane >> 3);
           xo[j] = (uint32_t)(min(tok, T - 1) * H * 2 + rs_chunk(j, lane) * 16);
         }
@@ -247,9 +252,12 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // lane parts of the LDS addresses of half step h; 16-row groups of a row
   // slice are whole 2 KiB apart (the swizzle only sees a row's low bits)
   // down: lane 4 c + m of group q reads row 32 h + 8 q + c (+ 4 for the
-  // second read) at columns 128 wn + 16 t + 4 m..+3 for A tile t, i.e. 16-byte
-  // chunk 16 wn + 2 t + m / 2, half m & 1.  Rows 32 h + 8 q + c and + 4 share
-  // their swizzle, so a lane's chunk for tile t is 16 wn + (dn_v ^ 2 t).
+  // second read) at columns 128 wn + 32 (t / 2) + 8 m + 4 (t % 2) .. + 3 for
+  // A tile t, i.e. 16-byte chunk 16 wn + 4 (t / 2) + m, half t % 2.  So tile
+  // t's MFMA row 4 q + c is column 128 wn + 32 (t / 2) + 8 q + 4 (t % 2) + c,
+  // and tiles 2 u, 2 u + 1 give each lane 8 consecutive columns (one 16-byte
+  // store).  Rows 32 h + 8 q + c and + 4 share their swizzle, so a lane's
+  // chunk for tile t is 16 wn + (dn_v ^ 4 (t / 2)).
   int lane_b[2], lane_a[2];
   int dn_v = 0;
 #pragma unroll
@@ -259,8 +267,8 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
       lane_a[h] = rs_addr(64 * wn + r16, 4 * h + q);
     } else {
       const int r = 32 * h + 8 * q + (r16 >> 2);
-      lane_a[h] = r * 512 + 256 * wn + 8 * (r16 & 1);
-      dn_v = ((r16 & 3) >> 1) ^ wd_swz(r);
+      lane_a[h] = r * 512 + 256 * wn;
+      dn_v = (r16 & 3) ^ wd_swz(r);
     }
   }
   auto half_step = [&](int g, int h) __attribute__((always_inline)) {
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint8_t* p = bw + ((dn_v ^ (2 * t)) << 4);
+        const uint8_t* p = bw + 8 * (t & 1) + ((dn_v ^ (4 * (t >> 1))) << 4);
         const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 512);
         A[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
@@ -296,9 +304,9 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // Every epilogue issues the same number of stores per wave (kStores), rows
   // past the tile's end going to trash (the padding rows of h_routed, whose
   // contents are never used), so that the ring's waits can count them.
-  // Each lane has its own 8 bytes of trash (blocks spread over the padding
+  // Each lane has its own 16 bytes of trash (blocks spread over the padding
   // rows), so the dropped stores do not all hit one line.
-  uint16_t* const trash = hrw_p + (size_t)T * K * I + (size_t)(blockIdx.x & 7) * 2048 + 4 * tid;
+  uint16_t* const trash = hrw_p + (size_t)T * K * I + (size_t)(blockIdx.x & 7) * 4096 + 8 * tid;
   auto epilogue = [&](int m) __attribute__((always_inline)) {
     const GTile g = gtile(tab_p, first + m * nbx, S);
     const bool sh = g.e >= E;
@@ -323,19 +331,21 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
         }
       }
     } else {
-      // tile t, C row 4 q + c: column 128 wn + 16 t + 4 q + c
+      // tiles 2 u, 2 u + 1: lane holds columns 128 wn + 32 u + 8 q + 0..7
       uint16_t* ob = orw_p + (sh ? sh_o : 0) +
-                     (size_t)(g.row0 + rr) * H + g.s * kDnOut + 128 * wn + 4 * q;
+                     (size_t)(g.row0 + rr) * H + g.s * kDnOut + 128 * wn + 8 * q;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const bool ok = rr + 16 * n < g.nrows;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          u32x2 pk;
-          pk.x = pack_bf16x2(acc[t][n][0], acc[t][n][1]);
-          pk.y = pack_bf16x2(acc[t][n][2], acc[t][n][3]);
-          uint16_t* dst = ok ? ob + (size_t)16 * n * H + 16 * t : trash;
-          store8(dst, pk);
+        for (int u = 0; u < 4; ++u) {
+          u32x4 pk;
+          pk.x = pack_bf16x2(acc[2 * u][n][0], acc[2 * u][n][1]);
+          pk.y = pack_bf16x2(acc[2 * u][n][2], acc[2 * u][n][3]);
+          pk.z = pack_bf16x2(acc[2 * u + 1][n][0], acc[2 * u + 1][n][1]);
+          pk.w = pack_bf16x2(acc[2 * u + 1][n][2], acc[2 * u + 1][n][3]);
+          uint16_t* dst = ok ? ob + (size_t)16 * n * H + 32 * u : trash;
+          *(__attribute__((address_space(1))) u32x4*)dst = pk;
         }
       }
     }

@@ -142,14 +142,22 @@ __global__ __launch_bounds__(256, 1) void k_gateup_stream(const ExpertArgs a, in
     const GItem it = item(m);
     pe = it.e;
     prow0 = it.row0;
+    // token rows 16 j + 4 w + lane / 16 of the item (rows past its end repeat
+    // its last row): scalar loads, which wait on lgkmcnt and never on the
+    // ring's vmcnt; each lane picks its row's value
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int tr = min(16 * (8 + j) + 4 * w + (lane >> 4) - 128, it.nrows - 1);
-      ptok[j] = it.e < E ? load_i32_async(sp_p + it.row0 + tr) : it.row0 + tr;
+      int32_t v = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int tr = min(16 * j + 4 * w + m, it.nrows - 1);
+        const int32_t sv = it.e < E ? sload(sp_p + it.row0 + tr) : it.row0 + tr;
+        v = (lane >> 4) == m ? sv : v;
+      }
+      ptok[j] = v;
     }
   };
   fetch_rows(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first item's rows, before any ring load
 
   // stage cursor: item m, stage kk of it
   int sm = -1, sk = 0;
@@ -164,10 +172,6 @@ __global__ __launch_bounds__(256, 1) void k_gateup_stream(const ExpertArgs a, in
       ub = reinterpret_cast<const uint8_t*>(uniform_ptr(wu_p + (sh ? sh_u : 0) + wofs));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        // rows prefetched a whole item (H / 128 >= 4 stages) ago: the ring
-        // waits since then, each leaving at most 22 loads outstanding while
-        // at least 10 were issued per stage, have covered them
-        settle(ptok[j]);
         const int r = 16 * (8 + j) + 4 * w + (lane >> 4);
         const int tok = pe < E ? ptok[j] / K : ptok[j];
         off[8 + j] = (uint32_t)(min(tok, T - 1) * H * 2 + (((lane & 15) ^ (r & 15)) << 4));

@@ -38,17 +38,6 @@ __device__ __forceinline__ void store8(uint16_t* p, u32x2 v) {
   *(__attribute__((address_space(1))) u32x2*)p = v;
 }
 
-// Vector load of one int32 issued as inline asm: the compiler then inserts no
-// wait for it (which would also wait for the ring's loads).  The caller reads
-// the value only after later ring waits have covered it, and passes it through
-// settle() there so that the read cannot move above them.
-__device__ __forceinline__ int32_t load_i32_async(const int32_t* p) {
-  int32_t v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ void settle(int32_t& v) { asm volatile("" : "+v"(v)); }
-
 // W_down slices (64 rows k x 512 B): 16-byte chunk c of row r sits at chunk
 // c ^ wd_swz(r).  The transpose reads of one instruction cover 16 rows
 // (8 q + c, q, c = 0..3) at one 32-byte column window; the XOR spreads them
