@@ -1,4 +1,5 @@
-"""CPU oracle of the group-limited top-k MoE layer forward -- TEST INFRASTRUCTURE.
+"""CPU oracle of the group-limited top-k MoE layer (forward, load balancing and
+the backward for a fixed routing) -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -7,7 +8,8 @@ its Python binding) never calls it and shares no code with it.
 The arithmetic lives in ``oracle.c`` (plain C, fp64, loops per token and per
 expert); this module only marshals numpy arrays.  Activations and expert
 weights are passed either as ``np.float32`` arrays or as bf16 bit patterns in
-``np.uint16`` arrays (numpy has no bf16 type).
+``np.uint16`` arrays (numpy has no bf16 type); the backward's functions also
+take ``np.float64`` arrays (the finite-difference pins perturb in fp64).
 
 Method source: the page "InternLumina-U2中256个专家的路由秘密：分组受限Top-K、
 Expert Bias与Fused MoE详解", sections 二 (sigmoid router, group-limited top-k,
@@ -16,6 +18,11 @@ balancing), 四 (stacked SwiGLU experts, eager per-expert loop and
 sort-by-expert inference), 五 (shared expert added unweighted), 六 (per-expert
 hit counts and their statistics); and the page at m.lqnn.cn/news/279712,
 section "MoE 负载均衡 Loss 别忘加" (the auxiliary loss E * sum_i f_i * P_i).
+
+The backward (chain rule written out in ``oracle.c``) is pinned by central
+finite differences of every input and weight, by torch.autograd applied to
+the same forward written with torch ops, and by identities of the forward's
+form (``tests/test_oracle_backward.py``).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 except the layer output's numeric value at full size, which no page prints
@@ -34,7 +41,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.environ.get("ORACLE_SO") or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 _lib = None
 
 
@@ -76,6 +83,13 @@ def _load():
     lib.orc_expert_stats.argtypes = [i32, i32, i32, P, P, P]
     lib.orc_bias_update.argtypes = [i32, P, P, P, ctypes.c_double]
     lib.orc_aux_loss.argtypes = [i32, i32, P, P, P, P, P]
+    d = ctypes.c_double
+    lib.orc_backward_tokens.argtypes = [P, i32, i32, P, i32, P, i32, P, P, d, P, P, i32,
+                                        P, P, P, P, i32]
+    lib.orc_backward_expert_weights.argtypes = [P, i32, i32, P, i32, P, P, d, P, i32, P, P, P,
+                                                i32]
+    lib.orc_router_weight_grad.argtypes = [i32, i32, i32, P, i32, P, P]
+    lib.orc_logits_any.argtypes = [i32, i32, i32, P, i32, P, i32, P]
     _lib = lib
     return lib
 
@@ -107,6 +121,8 @@ def _act(a: np.ndarray):
         return a, F32
     if a.dtype == np.uint16:
         return a, BF16
+    if a.dtype == np.float64:
+        return a, F64
     raise TypeError(f"expected float32 or uint16 (bf16 bits), got {a.dtype}")
 
 
@@ -344,3 +360,79 @@ def aux_loss(lam: np.ndarray, counts: np.ndarray):
     loss = np.empty(1, np.float64)
     _load().orc_aux_loss(T, E, _ptr(lam), _ptr(c), _ptr(f), _ptr(P), _ptr(loss))
     return f, P, float(loss[0])
+
+
+# --------------------------------------------------------------------------- backward
+
+def logits_any(x, w_router) -> np.ndarray:
+    """fp64 router logits from x and W_r of any dtype (fp32, bf16 bits, fp64)."""
+    x, xdt = _act(x)
+    wr, rdt = _act(w_router)
+    T, H = x.shape
+    E = wr.shape[0]
+    lam = np.empty((T, E), np.float64)
+    _load().orc_logits_any(T, H, E, _ptr(x), xdt, _ptr(wr), rdt, _ptr(lam))
+    return lam
+
+
+def backward_tokens(x, w_router, lam, idx, scale, dy, w_gate, w_up, w_down, ws_gate=None,
+                    ws_up=None, ws_down=None, tokens=None, want_y=False, nthreads=None):
+    """Per-token backward for a fixed routing: dict(dx, dweight, dlogit[, y])
+    for the rows ``tokens`` (all rows when None).  fp64, exact sigmoid."""
+    x, xdt = _act(x)
+    wr, rdt = _act(w_router)
+    T, H = x.shape
+    E = wr.shape[0]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    K = idx.shape[1]
+    lam = np.ascontiguousarray(lam, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    assert lam.shape == (T, E) and dy.shape == (T, H)
+    st, keep = _experts_struct(H, K, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = T if tok is None else tok.size
+    dx = np.empty((n, H), np.float64)
+    dw = np.empty((n, K), np.float64)
+    dl = np.empty((n, E), np.float64)
+    y = np.empty((n, H), np.float64) if want_y else None
+    _load().orc_backward_tokens(ctypes.byref(st), T, E, _ptr(x), xdt, _ptr(wr), rdt, _ptr(lam),
+                                _ptr(idx), float(scale), _ptr(dy), _ptr(tok), n, _ptr(dx),
+                                _ptr(dw), _ptr(dl), _ptr(y), nthreads or default_threads())
+    del keep
+    out = dict(dx=dx, dweight=dw, dlogit=dl)
+    if want_y:
+        out["y"] = y
+    return out
+
+
+def backward_expert_weights(x, lam, idx, scale, dy, e, w_gate, w_up, w_down, ws_gate=None,
+                            ws_up=None, ws_down=None, nthreads=None):
+    """(dW_gate, dW_up, dW_down) of expert e ([I][H] each; e == E: the shared
+    expert, [I_shared][H]) for a fixed routing, fp64."""
+    x, xdt = _act(x)
+    T, H = x.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    K = idx.shape[1]
+    lam = np.ascontiguousarray(lam, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    st, keep = _experts_struct(H, K, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    E = st.E
+    I = st.I_shared if e >= E else st.I
+    assert I > 0
+    out = [np.empty((I, H), np.float64) for _ in range(3)]
+    _load().orc_backward_expert_weights(ctypes.byref(st), T, E, _ptr(x), xdt, _ptr(lam),
+                                        _ptr(idx), float(scale), _ptr(dy), int(e),
+                                        *[_ptr(o) for o in out], nthreads or default_threads())
+    del keep
+    return tuple(out)
+
+
+def router_weight_grad(x, dlogit) -> np.ndarray:
+    """dW_r [E][H] = dlogit^T x, fp64, summed over tokens in order."""
+    x, xdt = _act(x)
+    T, H = x.shape
+    dl = np.ascontiguousarray(dlogit, dtype=np.float64)
+    E = dl.shape[1]
+    out = np.empty((E, H), np.float64)
+    _load().orc_router_weight_grad(T, E, H, _ptr(x), xdt, _ptr(dl), _ptr(out))
+    return out

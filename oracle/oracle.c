@@ -33,6 +33,7 @@ static double bf16_bits_to_double(uint16_t b) {
 
 static double elem(const void* base, int dt, size_t i) {
   if (dt == ORC_BF16) return bf16_bits_to_double(((const uint16_t*)base)[i]);
+  if (dt == ORC_F64) return ((const double*)base)[i];
   return (double)((const float*)base)[i];
 }
 
@@ -778,4 +779,321 @@ void orc_aux_loss(int T, int E, const float* lam, const int32_t* counts, double*
   }
   *loss = (double)E * acc;
   free(p);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the layer for a fixed routing                                */
+/* ------------------------------------------------------------------------ */
+/* The layer's output as a function of its inputs and weights, with the
+ * chosen experts held fixed (the choice is piecewise constant in the inputs,
+ * so it carries no gradient; the expert bias only enters the choice and so
+ * has none either):
+ *   lam[t][e] = sum_h x[t][h] * W_r[e][h]                        [Routing §二 step 1]
+ *   s = 1 / (1 + exp(-lam))                                       (the logistic sigmoid)
+ *   w_j = scale * s_{idx_j} / (sum_k s_{idx_k} + 1e-20)           [Routing §二 step 3]
+ *   y[t] = shared(x[t]) + sum_j w_j * expert_{idx_j}(x[t])        [Routing §四, §五]
+ *   expert(x) = down(silu(gate x) * (up x)), silu(z) = z / (1 + exp(-z))
+ * and, for an upstream gradient dy, the loss L = sum_{t,h} dy[t][h] * y[t][h].
+ * Everything here is fp64 with the exact logistic function (the forward's
+ * fp32 rounding of the scores is not part of what is differentiated).  The
+ * derivatives, written out step by step below, follow from the chain rule:
+ *   dL/dw_j   = <dy, expert_j(x)>,  d_o = w_j * dy (the expert's output grad)
+ *   d_a_i     = sum_h W_down[i][h] * d_o_h;  dW_down[i][h] += a_i * d_o_h
+ *   d_g_i     = d_a_i * u_i * silu'(g_i),  silu'(g) = sig(g) * (1 + g * (1 - sig(g)))
+ *   d_u_i     = d_a_i * silu(g_i)
+ *   dW_gate[i][h] += d_g_i * x_h,  dW_up[i][h] += d_u_i * x_h
+ *   dx_h     += sum_i d_g_i * W_gate[i][h] + d_u_i * W_up[i][h]
+ *   dL/ds_m   = scale / D * (dL/dw_m - sum_j dL/dw_j * s_j / D),  D = sum s + 1e-20
+ *               (quotient rule; m over the chosen experts)
+ *   dL/dlam_m = dL/ds_m * s_m * (1 - s_m) (chosen m; 0 for the others)
+ *   dW_r[m][h] += dL/dlam_m * x_h,  dx_h += sum_m dL/dlam_m * W_r[m][h]   */
+
+static double logistic(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* One expert on one token row: g, u, a (= silu(g) u) and the output o. */
+static void expert_fwd(const void* wg, const void* wu, const void* wd, int wdt, size_t base, int I,
+                       int H, const double* xr, double* g, double* u, double* a, double* o) {
+  for (int i = 0; i < I; ++i) {
+    size_t row = base + (size_t)i * H;
+    double gi = 0.0, ui = 0.0;
+    for (int h = 0; h < H; ++h) gi += xr[h] * elem(wg, wdt, row + h);
+    for (int h = 0; h < H; ++h) ui += xr[h] * elem(wu, wdt, row + h);
+    g[i] = gi;
+    u[i] = ui;
+    a[i] = gi * logistic(gi) * ui;
+  }
+  if (o) {
+    for (int h = 0; h < H; ++h) o[h] = 0.0;
+    for (int i = 0; i < I; ++i) {
+      size_t row = base + (size_t)i * H;
+      for (int h = 0; h < H; ++h) o[h] += a[i] * elem(wd, wdt, row + h);
+    }
+  }
+}
+
+/* Given d_o (the gradient of the expert's output), the gradients of g and u. */
+static void expert_bwd_act(const void* wd, int wdt, size_t base, int I, int H, const double* d_o,
+                           const double* g, const double* u, double* dg, double* du) {
+  for (int i = 0; i < I; ++i) {
+    size_t row = base + (size_t)i * H;
+    double da = 0.0;
+    for (int h = 0; h < H; ++h) da += elem(wd, wdt, row + h) * d_o[h];
+    double sg = logistic(g[i]);
+    double silu = g[i] * sg;
+    double dsilu = sg * (1.0 + g[i] * (1.0 - sg));
+    dg[i] = da * u[i] * dsilu;
+    du[i] = da * silu;
+  }
+}
+
+/* The chosen experts' scores and the routing weights of one token. */
+static double token_weights(int K, const int32_t* idx, const double* lam, double scale, double* s,
+                            double* w) {
+  double S = 0.0;
+  for (int j = 0; j < K; ++j) {
+    s[j] = logistic(lam[idx[j]]);
+    S += s[j];
+  }
+  double D = S + 1e-20;
+  for (int j = 0; j < K; ++j) w[j] = scale * s[j] / D;
+  return D;
+}
+
+typedef struct {
+  const orc_experts_t* ex;
+  int T, E, rdt, xdt;
+  const void* x;
+  const void* w_router;
+  const double* lam;
+  const int32_t* idx;
+  double scale;
+  const double* dy;
+  const int32_t* tokens;
+  double *dx, *dweight, *dlogit, *y;
+} bwd_tok_ctx_t;
+
+static void bwd_tokens_range(void* vctx, int r0, int r1) {
+  bwd_tok_ctx_t* c = (bwd_tok_ctx_t*)vctx;
+  const orc_experts_t* ex = c->ex;
+  int H = ex->H, I = ex->I, Is = ex->I_shared, K = ex->K, E = c->E;
+  int amax = I > Is ? I : Is;
+  if (amax < 1) amax = 1;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+  double* g = (double*)malloc(sizeof(double) * (size_t)amax);
+  double* u = (double*)malloc(sizeof(double) * (size_t)amax);
+  double* a = (double*)malloc(sizeof(double) * (size_t)amax);
+  double* dg = (double*)malloc(sizeof(double) * (size_t)amax);
+  double* du = (double*)malloc(sizeof(double) * (size_t)amax);
+  double* o = (double*)malloc(sizeof(double) * (size_t)H);
+  double* d_o = (double*)malloc(sizeof(double) * (size_t)H);
+  double* s = (double*)malloc(sizeof(double) * (size_t)K);
+  double* wj = (double*)malloc(sizeof(double) * (size_t)K);
+  double* gw = (double*)malloc(sizeof(double) * (size_t)K);
+  for (int r = r0; r < r1; ++r) {
+    int t = c->tokens ? c->tokens[r] : r;
+    const double* dy = c->dy + (size_t)t * H;
+    const int32_t* it = c->idx + (size_t)t * K;
+    double* dx = c->dx ? c->dx + (size_t)r * H : NULL;
+    double* yr = c->y ? c->y + (size_t)r * H : NULL;
+    for (int h = 0; h < H; ++h) xr[h] = elem(c->x, c->xdt, (size_t)t * H + h);
+    if (dx)
+      for (int h = 0; h < H; ++h) dx[h] = 0.0;
+    if (yr)
+      for (int h = 0; h < H; ++h) yr[h] = 0.0;
+    double D = token_weights(K, it, c->lam + (size_t)t * E, c->scale, s, wj);
+    /* shared expert, weight 1 */
+    if (Is > 0 && ex->ws_gate) {
+      expert_fwd(ex->ws_gate, ex->ws_up, ex->ws_down, ex->wdt, 0, Is, H, xr, g, u, a, o);
+      if (yr)
+        for (int h = 0; h < H; ++h) yr[h] += o[h];
+      if (dx) {
+        expert_bwd_act(ex->ws_down, ex->wdt, 0, Is, H, dy, g, u, dg, du);
+        for (int i = 0; i < Is; ++i)
+          for (int h = 0; h < H; ++h)
+            dx[h] += dg[i] * elem(ex->ws_gate, ex->wdt, (size_t)i * H + h) +
+                     du[i] * elem(ex->ws_up, ex->wdt, (size_t)i * H + h);
+      }
+    }
+    /* routed experts, in j order */
+    for (int j = 0; j < K; ++j) {
+      size_t base = (size_t)it[j] * I * H;
+      expert_fwd(ex->w_gate, ex->w_up, ex->w_down, ex->wdt, base, I, H, xr, g, u, a, o);
+      double d = 0.0;
+      for (int h = 0; h < H; ++h) d += dy[h] * o[h];
+      gw[j] = d;
+      if (yr)
+        for (int h = 0; h < H; ++h) yr[h] += wj[j] * o[h];
+      if (dx) {
+        for (int h = 0; h < H; ++h) d_o[h] = wj[j] * dy[h];
+        expert_bwd_act(ex->w_down, ex->wdt, base, I, H, d_o, g, u, dg, du);
+        for (int i = 0; i < I; ++i)
+          for (int h = 0; h < H; ++h)
+            dx[h] += dg[i] * elem(ex->w_gate, ex->wdt, base + (size_t)i * H + h) +
+                     du[i] * elem(ex->w_up, ex->wdt, base + (size_t)i * H + h);
+      }
+    }
+    /* router: quotient rule through the normalised weights, then the sigmoid */
+    double sgs = 0.0;
+    for (int j = 0; j < K; ++j) sgs += gw[j] * s[j];
+    double* dl = c->dlogit ? c->dlogit + (size_t)r * E : NULL;
+    if (dl)
+      for (int e = 0; e < E; ++e) dl[e] = 0.0;
+    for (int j = 0; j < K; ++j) {
+      double ds = c->scale / D * (gw[j] - sgs / D);
+      double dlam = ds * s[j] * (1.0 - s[j]);
+      if (dl) dl[it[j]] = dlam;
+      if (dx)
+        for (int h = 0; h < H; ++h)
+          dx[h] += dlam * elem(c->w_router, c->rdt, (size_t)it[j] * H + h);
+    }
+    if (c->dweight)
+      for (int j = 0; j < K; ++j) c->dweight[(size_t)r * K + j] = gw[j];
+  }
+  free(xr); free(g); free(u); free(a); free(dg); free(du); free(o); free(d_o);
+  free(s); free(wj); free(gw);
+}
+
+void orc_backward_tokens(const orc_experts_t* ex, int T, int E, const void* x, int xdt,
+                         const void* w_router, int rdt, const double* lam, const int32_t* idx,
+                         double scale, const double* dy, const int32_t* tokens, int n_tok,
+                         double* dx, double* dweight, double* dlogit, double* y, int nthreads) {
+  bwd_tok_ctx_t c = {ex, T, E, rdt, xdt, x, w_router, lam, idx, scale, dy, tokens,
+                     dx, dweight, dlogit, y};
+  parallel_range(bwd_tokens_range, &c, n_tok, nthreads);
+}
+
+/* Weight gradients of one expert (e < E: routed, over its pairs in token
+ * order; e == E: the shared expert, over every token).  The per-pair vectors
+ * a, d_o, d_g, d_u are formed first (in parallel over pairs), then each
+ * gradient row is summed over the pairs in order (in parallel over rows). */
+typedef struct {
+  const orc_experts_t* ex;
+  int E, xdt, np, e;
+  const void* x;
+  const double* lam;
+  const int32_t* idx;
+  double scale;
+  const double* dy;
+  const int32_t* ptok; /* token of each pair */
+  const int32_t* pj;   /* slot j of each pair (-1: shared) */
+  double *A, *DO, *DG, *DU;
+} bwd_pair_ctx_t;
+
+static void bwd_pairs_range(void* vctx, int p0, int p1) {
+  bwd_pair_ctx_t* c = (bwd_pair_ctx_t*)vctx;
+  const orc_experts_t* ex = c->ex;
+  int H = ex->H, K = ex->K;
+  int shared = c->e >= c->E;
+  int I = shared ? ex->I_shared : ex->I;
+  const void* wg = shared ? ex->ws_gate : ex->w_gate;
+  const void* wu = shared ? ex->ws_up : ex->w_up;
+  const void* wd = shared ? ex->ws_down : ex->w_down;
+  size_t base = shared ? 0 : (size_t)c->e * I * H;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+  double* g = (double*)malloc(sizeof(double) * (size_t)I);
+  double* u = (double*)malloc(sizeof(double) * (size_t)I);
+  double* s = (double*)malloc(sizeof(double) * (size_t)K);
+  double* wj = (double*)malloc(sizeof(double) * (size_t)K);
+  for (int p = p0; p < p1; ++p) {
+    int t = c->ptok[p];
+    for (int h = 0; h < H; ++h) xr[h] = elem(c->x, c->xdt, (size_t)t * H + h);
+    double w = 1.0;
+    if (!shared) {
+      token_weights(K, c->idx + (size_t)t * K, c->lam + (size_t)t * c->E, c->scale, s, wj);
+      w = wj[c->pj[p]];
+    }
+    double* a = c->A + (size_t)p * I;
+    double* d_o = c->DO + (size_t)p * H;
+    expert_fwd(wg, wu, wd, ex->wdt, base, I, H, xr, g, u, a, NULL);
+    for (int h = 0; h < H; ++h) d_o[h] = w * c->dy[(size_t)t * H + h];
+    expert_bwd_act(wd, ex->wdt, base, I, H, d_o, g, u, c->DG + (size_t)p * I,
+                   c->DU + (size_t)p * I);
+  }
+  free(xr); free(g); free(u); free(s); free(wj);
+}
+
+typedef struct {
+  int H, I, np, xdt;
+  const void* x;
+  const int32_t* ptok;
+  const double *A, *DO, *DG, *DU;
+  double *dwg, *dwu, *dwd;
+} bwd_rows_ctx_t;
+
+static void bwd_rows_range(void* vctx, int i0, int i1) {
+  bwd_rows_ctx_t* c = (bwd_rows_ctx_t*)vctx;
+  int H = c->H, I = c->I;
+  for (int i = i0; i < i1; ++i) {
+    double* rg = c->dwg + (size_t)i * H;
+    double* ru = c->dwu + (size_t)i * H;
+    double* rd = c->dwd + (size_t)i * H;
+    for (int h = 0; h < H; ++h) rg[h] = ru[h] = rd[h] = 0.0;
+    for (int p = 0; p < c->np; ++p) {
+      int t = c->ptok[p];
+      double ai = c->A[(size_t)p * I + i];
+      double gi = c->DG[(size_t)p * I + i];
+      double ui = c->DU[(size_t)p * I + i];
+      const double* d_o = c->DO + (size_t)p * H;
+      for (int h = 0; h < H; ++h) {
+        double xh = elem(c->x, c->xdt, (size_t)t * H + h);
+        rg[h] += gi * xh;
+        ru[h] += ui * xh;
+        rd[h] += ai * d_o[h];
+      }
+    }
+  }
+}
+
+void orc_backward_expert_weights(const orc_experts_t* ex, int T, int E, const void* x, int xdt,
+                                 const double* lam, const int32_t* idx, double scale,
+                                 const double* dy, int e, double* dwg, double* dwu, double* dwd,
+                                 int nthreads) {
+  int K = ex->K, H = ex->H;
+  int shared = e >= E;
+  int I = shared ? ex->I_shared : ex->I;
+  int np = 0;
+  int64_t P = (int64_t)T * K;
+  int32_t* ptok = (int32_t*)malloc(sizeof(int32_t) * (size_t)(shared ? (T > 0 ? T : 1) : (P > 0 ? P : 1)));
+  int32_t* pj = (int32_t*)malloc(sizeof(int32_t) * (size_t)(shared ? (T > 0 ? T : 1) : (P > 0 ? P : 1)));
+  if (shared) {
+    for (int t = 0; t < T; ++t) { ptok[np] = t; pj[np] = -1; ++np; }
+  } else {
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < K; ++j)
+        if (idx[(size_t)t * K + j] == e) { ptok[np] = t; pj[np] = j; ++np; }
+  }
+  size_t npp = np > 0 ? (size_t)np : 1;
+  double* A = (double*)malloc(sizeof(double) * npp * (size_t)I);
+  double* DG = (double*)malloc(sizeof(double) * npp * (size_t)I);
+  double* DU = (double*)malloc(sizeof(double) * npp * (size_t)I);
+  double* DO = (double*)malloc(sizeof(double) * npp * (size_t)H);
+  bwd_pair_ctx_t pc = {ex, E, xdt, np, e, x, lam, idx, scale, dy, ptok, pj, A, DO, DG, DU};
+  parallel_range(bwd_pairs_range, &pc, np, nthreads);
+  bwd_rows_ctx_t rc = {H, I, np, xdt, x, ptok, A, DO, DG, DU, dwg, dwu, dwd};
+  parallel_range(bwd_rows_range, &rc, I, nthreads);
+  free(ptok); free(pj); free(A); free(DG); free(DU); free(DO);
+}
+
+/* dW_r[e][h] = sum_t dlogit[t][e] * x[t][h], summed over t in order. */
+void orc_router_weight_grad(int T, int E, int H, const void* x, int xdt, const double* dlogit,
+                            double* dwr) {
+  for (size_t i = 0; i < (size_t)E * H; ++i) dwr[i] = 0.0;
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double d = dlogit[(size_t)t * E + e];
+      if (d == 0.0) continue;
+      for (int h = 0; h < H; ++h) dwr[(size_t)e * H + h] += d * elem(x, xdt, (size_t)t * H + h);
+    }
+}
+
+/* lam[t][e] = sum_h x[t][h] * W_r[e][h] in fp64 from inputs of any dtype. */
+void orc_logits_any(int T, int H, int E, const void* x, int xdt, const void* w_router, int rdt,
+                    double* lam) {
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += elem(x, xdt, (size_t)t * H + h) * elem(w_router, rdt, (size_t)e * H + h);
+      lam[(size_t)t * E + e] = acc;
+    }
 }

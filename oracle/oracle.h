@@ -25,7 +25,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
 
 /* sigma32: the fp32 logistic function as specified in oracle.c (fp64 Cody-Waite
  * exp + degree-13 Taylor, one division, one rounding to fp32). */
@@ -99,6 +99,30 @@ void orc_bias_update(int E, const int32_t* counts, const float* bias_in, float* 
                      double rate);
 void orc_aux_loss(int T, int E, const float* lam, const int32_t* counts, double* f, double* P,
                   double* loss);
+
+/* Backward of the layer for a fixed routing (definitions and the chain rule
+ * in oracle.c), fp64 with the exact logistic sigmoid.  lam [T][E] are the
+ * fp64 router logits; dy [T][H] the upstream gradient.
+ * orc_backward_tokens: for the rows tokens[0..n_tok) (all T when NULL):
+ *   dx [n_tok][H], dweight [n_tok][K] (dL/dw_j), dlogit [n_tok][E] (dL/dlam,
+ *   zero off the chosen experts) and, if y != NULL, the fixed-routing forward
+ *   y [n_tok][H]; any output may be NULL.
+ * orc_backward_expert_weights: dW_gate, dW_up, dW_down of expert e (e == E:
+ *   the shared expert), each [I][H] (I_shared for the shared expert).
+ * orc_router_weight_grad: dW_r [E][H] from dlogit [T][E].
+ * orc_logits_any: lam = x . W_r^T in fp64 (x, W_r of any ORC_ dtype). */
+void orc_backward_tokens(const orc_experts_t* ex, int T, int E, const void* x, int xdt,
+                         const void* w_router, int rdt, const double* lam, const int32_t* idx,
+                         double scale, const double* dy, const int32_t* tokens, int n_tok,
+                         double* dx, double* dweight, double* dlogit, double* y, int nthreads);
+void orc_backward_expert_weights(const orc_experts_t* ex, int T, int E, const void* x, int xdt,
+                                 const double* lam, const int32_t* idx, double scale,
+                                 const double* dy, int e, double* dwg, double* dwu, double* dwd,
+                                 int nthreads);
+void orc_router_weight_grad(int T, int E, int H, const void* x, int xdt, const double* dlogit,
+                            double* dwr);
+void orc_logits_any(int T, int H, int E, const void* x, int xdt, const void* w_router, int rdt,
+                    double* lam);
 
 #ifdef __cplusplus
 }

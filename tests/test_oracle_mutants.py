@@ -21,6 +21,8 @@ R = "tests/test_oracle_routing.py"
 X = "tests/test_oracle_experts.py"
 S = "tests/test_oracle_sigmoid.py"
 B = "tests/test_oracle_balance.py"
+D = "tests/test_oracle_backward.py"
+FD = D + "::test_every_gradient_matches_central_differences"
 
 MUTANTS = {
     "group_score_top1": ("  return m1 + m2;", "  return m1 + m1;", [R + "::test_brute_force_full_shape"]),
@@ -69,6 +71,17 @@ MUTANTS = {
     "aux_sigmoid_probs": ("      p[e] = exp((double)l[e] - m);", "      p[e] = 1.0 / (1.0 + exp(-(double)l[e]));",
                           [B + "::test_aux_loss_closed_form_one_large_logit"]),
     "sigmoid_sign": ("  double t = -(double)z;", "  double t = (double)z;", [S + "::test_textbook_values"]),
+    "bwd_silu_derivative_one_term": ("    double dsilu = sg * (1.0 + g[i] * (1.0 - sg));",
+                                     "    double dsilu = sg;", [FD]),
+    "bwd_quotient_rule_sign": ("      double ds = c->scale / D * (gw[j] - sgs / D);",
+                               "      double ds = c->scale / D * (gw[j] + sgs / D);", [FD]),
+    "bwd_up_grad_uses_gate": ("    du[i] = da * silu;", "    du[i] = da * g[i];", [FD]),
+    "bwd_no_sigmoid_slope": ("      double dlam = ds * s[j] * (1.0 - s[j]);",
+                             "      double dlam = ds * s[j];", [FD]),
+    "bwd_pairs_unweighted": ("      w = wj[c->pj[p]];", "      w = 1.0;", [FD]),
+    "bwd_down_grad_from_gate": ("        rd[h] += ai * d_o[h];", "        rd[h] += gi * d_o[h];", [FD]),
+    "bwd_router_grad_no_x": ("      for (int h = 0; h < H; ++h) dwr[(size_t)e * H + h] += d * elem(x, xdt, (size_t)t * H + h);",
+                             "      for (int h = 0; h < H; ++h) dwr[(size_t)e * H + h] += d;", [FD]),
 }
 
 
