@@ -25,7 +25,8 @@ EXPORTS = (
     "moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_layer_forward",
     "moe_residual_rmsnorm", "moe_status", "moe_sigmoid32", "moe_strerror",
     "moe_layer_forward_timed", "moe_stage_kernel", "moe_expert_stats", "moe_bias_update",
-    "moe_aux_loss_workspace_size", "moe_aux_loss",
+    "moe_aux_loss_workspace_size", "moe_aux_loss", "moe_backward_workspace_size",
+    "moe_layer_backward",
 )
 MOE_NSTAT = 8
 STAT_NAMES = ("hits", "max_load", "min_load", "cv", "idle", "hottest", "coldest",
@@ -95,6 +96,10 @@ def _load():
     lib.moe_aux_loss_workspace_size.restype = S
     lib.moe_aux_loss.argtypes = [i32, i32, P, P, P, P, P, P, S, P]
     lib.moe_aux_loss.restype = i
+    lib.moe_backward_workspace_size.argtypes = [D]
+    lib.moe_backward_workspace_size.restype = S
+    lib.moe_layer_backward.argtypes = [D, P, W, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.moe_layer_backward.restype = i
     lib.moe_strerror.argtypes = [i]
     lib.moe_strerror.restype = ctypes.c_char_p
     return lib
@@ -372,6 +377,55 @@ def moe_aux_loss(logits, counts, ws=None, out=None, stream=None):
     wp, wn = _ws(None, ws)
     _rc(LIB.moe_aux_loss(T, E, lp, cp, fp, pp, sp, wp, wn, _stream(stream)), "moe_aux_loss")
     return f, P, loss
+
+
+# ---------------------------------------------------------------------------- backward
+
+def backward_workspace(d: MoeDesc, device="cuda") -> torch.Tensor:
+    n = LIB.moe_backward_workspace_size(ctypes.byref(d))
+    if n == 0:
+        raise MoeError(-2, "moe_backward_workspace_size (invalid or unsupported desc)")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_layer_backward(d: MoeDesc, x, weights: dict, topk_idx, logits, dy, ws=None, out=None,
+                       stream=None):
+    """Gradients of sum(dy * y) for the routing topk_idx: returns dict(dx bf16
+    [T, H], dw_router fp32 [E, H], dw_gate / dw_up / dw_down fp32 [E, I, H],
+    dws_gate / dws_up / dws_down fp32 [I_shared, H] or None).  `out` may
+    supply those tensors."""
+    dev = x.device
+    T, H, E, K, I, Is = d.T, d.H, d.E, d.top_k, d.I, d.I_shared
+    dt = _act_dtype(d)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = dict(dx=torch.empty(T, H, dtype=dt, device=dev),
+                   dw_router=torch.empty(E, H, **f32), dw_gate=torch.empty(E, I, H, **f32),
+                   dw_up=torch.empty(E, I, H, **f32), dw_down=torch.empty(E, I, H, **f32),
+                   dws_gate=torch.empty(Is, H, **f32) if Is else None,
+                   dws_up=torch.empty(Is, H, **f32) if Is else None,
+                   dws_down=torch.empty(Is, H, **f32) if Is else None)
+    if ws is None:
+        ws = backward_workspace(d, dev)
+    W = _weights(d, weights, dev, need_router=True)
+    args = [
+        _check(x, "x", (T, H), dt, dev), ctypes.byref(W),
+        _check(topk_idx, "topk_idx", (T, K), torch.int32, dev),
+        _check(logits, "logits", (T, E), torch.float32, dev),
+        _check(dy, "dy", (T, H), dt, dev),
+        _check(out["dx"], "dx", (T, H), dt, dev),
+        _check(out["dw_router"], "dw_router", (E, H), torch.float32, dev),
+        _check(out["dw_gate"], "dw_gate", (E, I, H), torch.float32, dev),
+        _check(out["dw_up"], "dw_up", (E, I, H), torch.float32, dev),
+        _check(out["dw_down"], "dw_down", (E, I, H), torch.float32, dev),
+        _check(out["dws_gate"], "dws_gate", (Is, H), torch.float32, dev, optional=True),
+        _check(out["dws_up"], "dws_up", (Is, H), torch.float32, dev, optional=True),
+        _check(out["dws_down"], "dws_down", (Is, H), torch.float32, dev, optional=True),
+    ]
+    wp, wn = _ws(d, ws)
+    _rc(LIB.moe_layer_backward(ctypes.byref(d), *args, wp, wn, _stream(stream)),
+        "moe_layer_backward")
+    return out
 
 
 def moe_stack_forward(d: MoeDesc, x, layers, ws, eps: float = 1e-6, tracking=None,

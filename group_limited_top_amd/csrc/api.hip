@@ -212,9 +212,124 @@ int check_weights(const moe_desc_t& d, const moe_weights_t* W, bool need_router)
   return MOE_OK;
 }
 
+// Backward workspace regions.
+struct BwdLayout {
+  size_t status, counts, offsets, sorted_pair, pair_slot, perm, tile_off, tile_tab, inter, total;
+};
+
+BwdLayout make_bwd_layout(const moe_desc_t& d) {
+  const size_t T = (size_t)d.T, E = (size_t)d.E, P = T * (size_t)d.top_k;
+  BwdLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.status = take(kAlign);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted_pair = take(P * 4);
+  L.pair_slot = take(P * 4);
+  L.perm = take(moe::permute_scratch_ints((int64_t)P, d.E) * 4);
+  L.tile_off = take((E + 2) * 4);
+  L.tile_tab = take((size_t)moe::max_expert_tiles(d.T, d.top_k, d.E, d.I_shared,
+                                                  moe::kBwdTileRows) * 8);
+  L.inter = take(moe::bwd_intermediate_bytes(d.T, d.top_k, d.I, d.H, d.I_shared > 0));
+  L.total = o;
+  return L;
+}
+
+// The backward's envelope on top of the forward's: bf16, the shared expert
+// (if any) as wide as the routed ones.
+int validate_bwd(const moe_desc_t* d) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->I_shared != 0 && d->I_shared != d->I) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)(d->T * (int64_t)d->top_k + d->T) * d->H >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t moe_backward_workspace_size(const moe_desc_t* desc) {
+  if (validate_bwd(desc) != MOE_OK) return 0;
+  return make_bwd_layout(*desc).total;
+}
+
+int moe_layer_backward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                       const int32_t* topk_idx, const float* logits, const void* dy, void* dx,
+                       float* dw_router, float* dw_gate, float* dw_up, float* dw_down,
+                       float* dws_gate, float* dws_up, float* dws_down, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  int rc = validate_bwd(desc);
+  if (rc) return rc;
+  const moe_desc_t& d = *desc;
+  if (d.T == 0) return MOE_OK;
+  rc = check_weights(d, weights, true);
+  if (rc) return rc;
+  if (!x || !topk_idx || !logits || !dy || !dx || !dw_router || !dw_gate || !dw_up || !dw_down)
+    return MOE_ERR_INVALID;
+  const bool sh = d.I_shared > 0;
+  if (sh != (dws_gate != nullptr) || sh != (dws_up != nullptr) || sh != (dws_down != nullptr))
+    return MOE_ERR_INVALID;
+  if (dx == x || dx == dy) return MOE_ERR_INVALID;
+  const void* ps[] = {x, topk_idx, logits, dy, dx, dw_router, dw_gate, dw_up, dw_down,
+                      dws_gate, dws_up, dws_down};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  const BwdLayout L = make_bwd_layout(d);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (misaligned(ws)) return MOE_ERR_ALIGN;
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted_pair = at<int32_t>(ws, L.sorted_pair);
+  int32_t* pair_slot = at<int32_t>(ws, L.pair_slot);
+  int32_t* tile_off = at<int32_t>(ws, L.tile_off);
+  int32_t* tile_tab = at<int32_t>(ws, L.tile_tab);
+  rc = hip_rc(moe::launch_permute(topk_idx, (int64_t)d.T * d.top_k, d.E, d.T, d.I_shared,
+                                  moe::kBwdTileRows, at<int32_t>(ws, L.perm),
+                                  at<int32_t>(ws, L.counts), offsets, sorted_pair, pair_slot,
+                                  nullptr, tile_off, tile_tab, at<uint32_t>(ws, L.status),
+                                  stream));
+  if (rc) return rc;
+  moe::BwdInputs in;
+  in.T = d.T;
+  in.H = d.H;
+  in.E = d.E;
+  in.K = d.top_k;
+  in.I = d.I;
+  in.scale = d.routed_scaling_factor;
+  in.x = static_cast<const uint16_t*>(x);
+  in.dy = static_cast<const uint16_t*>(dy);
+  in.logits = logits;
+  in.idx = topk_idx;
+  in.w_router = weights->w_router;
+  in.wg = static_cast<const uint16_t*>(weights->w_gate);
+  in.wu = static_cast<const uint16_t*>(weights->w_up);
+  in.wd = static_cast<const uint16_t*>(weights->w_down);
+  in.swg = static_cast<const uint16_t*>(weights->ws_gate);
+  in.swu = static_cast<const uint16_t*>(weights->ws_up);
+  in.swd = static_cast<const uint16_t*>(weights->ws_down);
+  in.offsets = offsets;
+  in.sorted_pair = sorted_pair;
+  in.pair_slot = pair_slot;
+  in.tile_off = tile_off;
+  in.tile_tab = tile_tab;
+  in.scratch = at<void>(ws, L.inter);
+  in.dx = static_cast<uint16_t*>(dx);
+  in.dw_router = dw_router;
+  in.dwg = dw_gate;
+  in.dwu = dw_up;
+  in.dwd = dw_down;
+  in.dswg = dws_gate;
+  in.dswu = dws_up;
+  in.dswd = dws_down;
+  return hip_rc(moe::launch_backward(in, stream));
+}
+
 
 size_t moe_workspace_size(const moe_desc_t* desc) {
   if (validate(desc) != MOE_OK) return 0;

@@ -1,0 +1,446 @@
+// backward.hip -- backward of the MoE layer for the routing the forward chose.
+//
+// The layer ([Routing §二 steps 1-3, §四, §五]) with the chosen experts held
+// fixed (the choice is piecewise constant and carries no gradient; the expert
+// bias only enters the choice):
+//   s = sigmoid(lam), w_j = scale * s_j / (sum_k s_k + 1e-20) over the chosen
+//   experts, y = shared(x) + sum_j w_j * down(silu(gate x) * up x).
+// For an upstream gradient dy, with r = dy . W_down^T (per pair):
+//   dL/dw_j = <dy, expert_j(x)> = <a_j, r_j>  (a = silu(g) * u), d_a = w_j r_j,
+//   d_g = d_a * u * silu'(g), d_u = d_a * silu(g),
+//   dx   = sum over pairs of d_g . W_gate + d_u . W_up   (+ the shared expert)
+//          + sum_j dlam_j * W_r[e_j],
+//   dW_gate[e] = sum over e's pairs of d_g^T x, dW_up likewise with d_u,
+//   dW_down[e] = sum over e's pairs of (w_j a_j)^T dy,
+//   dlam_m = scale / D * (dL/dw_m - sum_j dL/dw_j s_j / D) * s_m (1 - s_m),
+//   dW_r[e] = sum over e's pairs of dlam * x.
+// Rows are the expert-sorted pairs (then the T shared rows), as in the forward.
+//
+// Steps: permute (the forward's kernels, 64-row tiles) -> k_bwd_gemm<kRowsNT>
+// (g = x W_g^T, u = x W_u^T, r = dy W_d^T, fp32) -> k_bwd_act (per row:
+// a, dL/dw, d_g, d_u, w a in bf16) -> k_bwd_router (per token: dlam) ->
+// k_bwd_gemm<kRowsNN> (per-row dx = d_g W_g + d_u W_u, bf16) ->
+// k_bwd_gemm<kWgrad> (dW_gate, dW_up, dW_down per expert, fp32, summed over
+// the expert's rows in order) -> k_bwd_router_wgrad (dW_r) -> k_bwd_combine
+// (dx per token: shared row, then the K pair rows in j order, then the router
+// terms in j order, fp32, one rounding).  Every sum has a fixed order: the
+// results are bit-reproducible.
+//
+// The GEMM tile: 64 x 64 outputs, 4 waves of 32 x 32 (2 x 2 MFMA 16x16x32
+// tiles), 32-deep K steps, operands staged in LDS (double buffer).  An operand
+// whose rows are K-contiguous in memory ("KC") is staged as [row][k] and read
+// with ds_read_b128; one stored [k][row] ("RC") is staged as is and read with
+// the gfx950 transpose read, which hands each lane 4 consecutive k of one row.
+#include "device.h"
+#include "expert_tiles.h"
+#include "kernels.h"
+#include "ring.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 64, kBN = 64, kBK = 32;
+constexpr int kBT = 256;  // threads per GEMM block
+
+enum BwdGemm { kRowsNT = 0, kRowsNN = 1, kWgrad = 2 };
+
+// KC staging: row r (of 64), 16-byte chunk c (of 4); chunk XOR (r / 4) % 4
+// spreads 16 rows read at one chunk over all 64 banks.
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// RC staging: k row (of 32), 16-byte chunk c (of 8); the XOR spreads the 16 k
+// rows one transpose read covers over 4 chunk pairs (2 rows each).
+__device__ __forceinline__ int rc_swz(int k) { return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)); }
+__device__ __forceinline__ int rc_off(int k, int c) { return k * 128 + ((c ^ rc_swz(k)) << 4); }
+
+__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+struct BwdArgs {
+  int T, H, E, K, I, P;  // P = T * K routed rows
+  float scale;
+  const uint16_t* x;     // [T][H]
+  const uint16_t* dy;    // [T][H]
+  const float* logits;   // [T][E]
+  const int32_t* idx;    // [T][K]
+  const float* w_router; // [E][H]
+  const uint16_t *wg, *wu, *wd;     // [E][I][H]
+  const uint16_t *swg, *swu, *swd;  // [I][H] (shared) or null
+  // permute
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted_pair;  // [P]
+  const int32_t* pair_slot;    // [P]
+  const int32_t* tile_off;     // [E+2]
+  const int32_t* tile_tab;     // row tiles {e | nrows << 16, row0}
+  // intermediates (rows: P routed in sorted order, then T shared)
+  float *g, *u, *r;            // [P+T][I]
+  uint16_t *dg, *du, *aw;      // [P+T][I] bf16
+  float* gw;                   // [P] dL/dw per pair id
+  float* dlam;                 // [P] dL/dlam per pair id
+  uint16_t* dxp;               // [P+T][H] bf16
+  // outputs
+  uint16_t* dx;                // [T][H]
+  float* dw_router;            // [E][H]
+  float *dwg, *dwu, *dwd;      // [E][I][H]
+  float *dswg, *dswu, *dswd;   // [I][H] or null
+};
+
+__device__ __forceinline__ void decode_row_tile(const BwdArgs& a, int t, int& e, int& row0,
+                                                int& nrows, int& orow) {
+  const int32_t v = a.tile_tab[2 * t];
+  e = v & 0xffff;
+  nrows = v >> 16;
+  row0 = a.tile_tab[2 * t + 1];
+  orow = e < a.E ? row0 : a.P + row0;  // row in the intermediates
+}
+
+// Fragment reads (lane (q, i) = (lane / 16, lane % 16)).
+__device__ __forceinline__ u32x4 read_kc(const uint8_t* buf, int r0, int lane) {
+  const int q = lane >> 4, i = lane & 15;
+  return lds16(buf + kc_off(r0 + i, q));
+}
+__device__ __forceinline__ u32x4 read_rc(const uint8_t* buf, int r0, int lane) {
+  // lane 4 c + m of group q points at k row 8 q + c, rows r0 + 4 m .. + 3
+  const int q = lane >> 4, i = lane & 15, c = i >> 2, m = i & 3;
+  const int k = 8 * q + c;
+  const int col = r0 + 4 * m;
+  const uint8_t* p = buf + k * 128 + (((col >> 3) ^ rc_swz(k)) << 4) + ((col & 4) << 1);
+  const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 128);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+}  // namespace
+
+// One 64 x 64 output tile.  MODE:
+//   kRowsNT: blockIdx.x = row tile, blockIdx.y = column tile over 3 I-wide
+//            segments: (x, W_g) -> g, (x, W_u) -> u, (dy, W_d) -> r; fp32 out.
+//            A rows gathered (token of each pair), B = weight rows; both KC.
+//   kRowsNN: blockIdx.x = row tile, blockIdx.y = column tile over H;
+//            K = 2 I: (d_g, W_g) then (d_u, W_u); A KC, B RC (weights
+//            [k][column]); bf16 out (per-row dx).
+//   kWgrad:  blockIdx.x = expert (E = shared), blockIdx.y = (I / 64) x (H / 64)
+//            tile, blockIdx.z = which: 0 dW_gate (d_g, x), 1 dW_up (d_u, x),
+//            2 dW_down (w a, dy); K = the expert's rows; A and B both RC
+//            (A^T: rows i of [m][i]; B: rows h of the gathered [m][h]).
+template <int MODE>
+__global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBM * kBK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[2][kBN * kBK * 2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int H = a.H, I = a.I, K = a.K, E = a.E;
+
+  int e = 0, row0 = 0, nrows = 0, orow = 0, n0 = 0, seg = 0, kdim = 0;
+  if (MODE == kWgrad) {
+    e = blockIdx.x;
+    const int it = (int)blockIdx.y / (H / kBN), ht = (int)blockIdx.y % (H / kBN);
+    row0 = it * kBM;  // i range of the output
+    n0 = ht * kBN;    // h range
+    seg = blockIdx.z;
+    if (e < E) {
+      orow = a.offsets[e];
+      kdim = a.offsets[e + 1] - orow;
+    } else {
+      if (!a.swg) return;
+      orow = a.P;
+      kdim = a.T;
+    }
+  } else {
+    if ((int)blockIdx.x >= a.tile_off[E + 1]) return;  // past the real tile count
+    decode_row_tile(a, blockIdx.x, e, row0, nrows, orow);
+    if (MODE == kRowsNT) {
+      const int per = I / kBN;
+      seg = (int)blockIdx.y / per;
+      n0 = ((int)blockIdx.y % per) * kBN;
+      kdim = H;
+    } else {
+      n0 = (int)blockIdx.y * kBN;
+      kdim = 2 * I;
+    }
+  }
+  const bool sh = e >= E;
+  const size_t ebase = sh ? 0 : (size_t)e * I * H;
+
+  // staging assignment: KC: row tid / 4, chunk tid % 4; RC: k row tid / 8, chunk tid % 8
+  const int kc_r = tid >> 2, kc_c = tid & 3;
+  const int rc_k = tid >> 3, rc_c = tid & 7;
+  // A (KC) row source for kRowsNT / kRowsNN
+  const uint16_t* a_row = nullptr;
+  const uint16_t* a_row2 = nullptr;  // kRowsNN: d_u row
+  const uint16_t* b_row = nullptr;   // kRowsNT: weight row
+  if (MODE == kRowsNT) {
+    const int m = min(kc_r, nrows - 1);
+    const int tok = sh ? row0 + m : a.sorted_pair[row0 + m] / K;
+    a_row = (seg < 2 ? a.x : a.dy) + (size_t)tok * H;
+    const uint16_t* wsrc = seg == 0 ? (sh ? a.swg : a.wg) : seg == 1 ? (sh ? a.swu : a.wu)
+                                                                      : (sh ? a.swd : a.wd);
+    b_row = wsrc + ebase + (size_t)(n0 + kc_r) * H;
+  } else if (MODE == kRowsNN) {
+    const int m = min(kc_r, nrows - 1);
+    a_row = a.dg + (size_t)(orow + m) * I;
+    a_row2 = a.du + (size_t)(orow + m) * I;
+  }
+
+  auto load = [&](int k0, u32x4& va, u32x4& vb) __attribute__((always_inline)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (MODE == kRowsNT) {
+      va = ld16(a_row + k0 + 8 * kc_c);
+      vb = ld16(b_row + k0 + 8 * kc_c);
+    } else if (MODE == kRowsNN) {
+      const bool second = k0 >= I;
+      const int kk = second ? k0 - I : k0;
+      va = ld16((second ? a_row2 : a_row) + kk + 8 * kc_c);
+      const uint16_t* w = (second ? (sh ? a.swu : a.wu) : (sh ? a.swg : a.wg)) + ebase;
+      vb = ld16(w + (size_t)(kk + rc_k) * H + n0 + 8 * rc_c);
+    } else {
+      const int m = k0 + rc_k;  // row of the expert (k of the GEMM)
+      if (m < kdim) {
+        const uint16_t* asrc = seg == 0 ? a.dg : seg == 1 ? a.du : a.aw;
+        va = ld16(asrc + (size_t)(orow + m) * I + row0 + 8 * rc_c);
+        const int tok = sh ? m : a.sorted_pair[orow + m] / K;
+        vb = ld16((seg < 2 ? a.x : a.dy) + (size_t)tok * H + n0 + 8 * rc_c);
+      } else {
+        va = z;
+        vb = z;
+      }
+    }
+  };
+  auto stage = [&](int buf, const u32x4& va, const u32x4& vb) __attribute__((always_inline)) {
+    if (MODE == kRowsNT) {
+      st16(sa[buf] + kc_off(kc_r, kc_c), va);
+      st16(sb[buf] + kc_off(kc_r, kc_c), vb);
+    } else if (MODE == kRowsNN) {
+      st16(sa[buf] + kc_off(kc_r, kc_c), va);
+      st16(sb[buf] + rc_off(rc_k, rc_c), vb);
+    } else {
+      st16(sa[buf] + rc_off(rc_k, rc_c), va);
+      st16(sb[buf] + rc_off(rc_k, rc_c), vb);
+    }
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (kdim + kBK - 1) / kBK;
+  u32x4 va, vb;
+  if (nk > 0) {
+    load(0, va, vb);
+    stage(0, va, vb);
+  }
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nk) load((s + 1) * kBK, va, vb);
+    u32x4 fa[2], fb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int ra = 32 * wm + 16 * t, rb = 32 * wn + 16 * t;
+      fa[t] = MODE == kWgrad ? read_rc(sa[buf], ra, lane) : read_kc(sa[buf], ra, lane);
+      fb[t] = MODE == kRowsNT ? read_kc(sb[buf], rb, lane) : read_rc(sb[buf], rb, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+    if (s + 1 < nk) stage(buf ^ 1, va, vb);
+    __syncthreads();
+  }
+
+  // C[A row 16 i + 4 q + c][B row 16 j + r16] of the wave's 32 x 32
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int ar = 32 * wm + 16 * i + 4 * q + c;  // A row in the tile
+        const int bc = 32 * wn + 16 * j + r16;         // B row in the tile
+        const float v = acc[i][j][c];
+        if (MODE == kRowsNT) {
+          if (ar < nrows) {
+            float* out = seg == 0 ? a.g : seg == 1 ? a.u : a.r;
+            out[(size_t)(orow + ar) * I + n0 + bc] = v;
+          }
+        } else if (MODE == kRowsNN) {
+          if (ar < nrows)
+            a.dxp[(size_t)(orow + ar) * H + n0 + bc] = (uint16_t)f32_to_bf16_bits(v);
+        } else {
+          float* out = sh ? (seg == 0 ? a.dswg : seg == 1 ? a.dswu : a.dswd)
+                          : (seg == 0 ? a.dwg : seg == 1 ? a.dwu : a.dwd) + ebase;
+          out[(size_t)(row0 + ar) * H + n0 + bc] = v;
+        }
+      }
+}
+
+// Per row (one wave): a = silu(g) u, dL/dw = <a, r> (routed rows), d_a = w r,
+// d_g = d_a u silu'(g), d_u = d_a silu(g), w a; w = 1 for the shared rows.
+__global__ __launch_bounds__(256) void k_bwd_act(const BwdArgs a, int nrows_total) {
+  const int lane = threadIdx.x & 63;
+  const int row = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows_total) return;
+  const int I = a.I, K = a.K, E = a.E;
+  // routed rows past offsets[E] exist only for pairs the permute skipped (an
+  // index outside [0, E)): nothing to compute there
+  if (row < a.P && row >= a.offsets[E]) return;
+  float w = 1.0f;
+  int p = -1;
+  if (row < a.P) {
+    p = a.sorted_pair[row];
+    const int t = p / K, j = p - (p / K) * K;
+    // the token's routing weights from its chosen experts' logits, j order
+    float S = 0.0f, sj = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const float s = sigm(a.logits[(size_t)t * E + min(max(a.idx[(size_t)t * K + k], 0), E - 1)]);
+      S += s;
+      if (k == j) sj = s;
+    }
+    w = a.scale * (sj / (S + 1e-20f));
+  }
+  const size_t base = (size_t)row * I;
+  float dot = 0.0f;
+  for (int i = lane; i < I; i += 64) {
+    const float g = a.g[base + i], u = a.u[base + i], r = a.r[base + i];
+    const float sg = sigm(g);
+    const float silu = g * sg;
+    const float act = silu * u;
+    dot += act * r;
+    const float da = w * r;
+    a.dg[base + i] = (uint16_t)f32_to_bf16_bits(da * u * (sg * (1.0f + g * (1.0f - sg))));
+    a.du[base + i] = (uint16_t)f32_to_bf16_bits(da * silu);
+    a.aw[base + i] = (uint16_t)f32_to_bf16_bits(w * act);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) dot += __shfl_xor(dot, o, 64);
+  if (p >= 0 && lane == 0) a.gw[p] = dot;
+}
+
+// Per token: dlam of its K chosen experts (quotient rule, then the sigmoid's slope).
+__global__ __launch_bounds__(256) void k_bwd_router(const BwdArgs a) {
+  const int t = (int)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  const int K = a.K, E = a.E;
+  float s[16], S = 0.0f, sgs = 0.0f;
+  for (int j = 0; j < K; ++j) {
+    s[j] = sigm(a.logits[(size_t)t * E + min(max(a.idx[(size_t)t * K + j], 0), E - 1)]);
+    S += s[j];
+  }
+  const float D = S + 1e-20f;
+  for (int j = 0; j < K; ++j) sgs += a.gw[(size_t)t * K + j] * s[j];
+  for (int j = 0; j < K; ++j) {
+    const float ds = a.scale / D * (a.gw[(size_t)t * K + j] - sgs / D);
+    a.dlam[(size_t)t * K + j] = ds * s[j] * (1.0f - s[j]);
+  }
+}
+
+// dW_r[e][h] = sum over e's pairs (sorted order) of dlam * x[token][h].
+__global__ __launch_bounds__(256) void k_bwd_router_wgrad(const BwdArgs a) {
+  const int e = blockIdx.x, h = (int)blockIdx.y * 256 + threadIdx.x;
+  if (h >= a.H) return;
+  const int m0 = a.offsets[e], m1 = a.offsets[e + 1];
+  float acc = 0.0f;
+  for (int m = m0; m < m1; ++m) {
+    const int p = a.sorted_pair[m];
+    acc += a.dlam[p] * bf16_to_f32(a.x[(size_t)(p / a.K) * a.H + h]);
+  }
+  a.dw_router[(size_t)e * a.H + h] = acc;
+}
+
+// dx[t] = shared row + pair rows in j order + router terms in j order.
+__global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
+  const int t = blockIdx.x;
+  const int H = a.H, K = a.K;
+  for (int h = threadIdx.x; h < H; h += 256) {
+    float acc = a.swg ? bf16_to_f32(a.dxp[(size_t)(a.P + t) * H + h]) : 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const int slot = a.pair_slot[(size_t)t * K + j];  // -1: a skipped pair
+      if (slot >= 0) acc += bf16_to_f32(a.dxp[(size_t)slot * H + h]);
+    }
+    for (int j = 0; j < K; ++j) {
+      const int e = min(max(a.idx[(size_t)t * K + j], 0), a.E - 1);
+      acc += a.dlam[(size_t)t * K + j] * a.w_router[(size_t)e * H + h];
+    }
+    a.dx[(size_t)t * H + h] = (uint16_t)f32_to_bf16_bits(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+size_t bwd_intermediate_bytes(int64_t T, int K, int I, int H, bool shared) {
+  const size_t rows = (size_t)(T * K + (shared ? T : 0));
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  return 3 * al(rows * I * 4) + 3 * al(rows * I * 2) + 2 * al((size_t)T * K * 4) +
+         al(rows * H * 2);
+}
+
+hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
+  BwdArgs a;
+  a.T = in.T;
+  a.H = in.H;
+  a.E = in.E;
+  a.K = in.K;
+  a.I = in.I;
+  a.P = in.T * in.K;
+  a.scale = in.scale;
+  a.x = in.x;
+  a.dy = in.dy;
+  a.logits = in.logits;
+  a.idx = in.idx;
+  a.w_router = in.w_router;
+  a.wg = in.wg;
+  a.wu = in.wu;
+  a.wd = in.wd;
+  a.swg = in.swg;
+  a.swu = in.swu;
+  a.swd = in.swd;
+  a.offsets = in.offsets;
+  a.sorted_pair = in.sorted_pair;
+  a.pair_slot = in.pair_slot;
+  a.tile_off = in.tile_off;
+  a.tile_tab = in.tile_tab;
+  a.dx = in.dx;
+  a.dw_router = in.dw_router;
+  a.dwg = in.dwg;
+  a.dwu = in.dwu;
+  a.dwd = in.dwd;
+  a.dswg = in.dswg;
+  a.dswu = in.dswu;
+  a.dswd = in.dswd;
+  const bool shared = in.swg != nullptr;
+  const int64_t rows = (int64_t)a.P + (shared ? a.T : 0);
+  uint8_t* p = reinterpret_cast<uint8_t*>(in.scratch);
+  auto take = [&](size_t bytes) {
+    uint8_t* q = p;
+    p += (bytes + 255) / 256 * 256;
+    return q;
+  };
+  a.g = reinterpret_cast<float*>(take((size_t)rows * a.I * 4));
+  a.u = reinterpret_cast<float*>(take((size_t)rows * a.I * 4));
+  a.r = reinterpret_cast<float*>(take((size_t)rows * a.I * 4));
+  a.dg = reinterpret_cast<uint16_t*>(take((size_t)rows * a.I * 2));
+  a.du = reinterpret_cast<uint16_t*>(take((size_t)rows * a.I * 2));
+  a.aw = reinterpret_cast<uint16_t*>(take((size_t)rows * a.I * 2));
+  a.gw = reinterpret_cast<float*>(take((size_t)a.P * 4));
+  a.dlam = reinterpret_cast<float*>(take((size_t)a.P * 4));
+  a.dxp = reinterpret_cast<uint16_t*>(take((size_t)rows * a.H * 2));
+
+  // row tiles: a host upper bound; blocks past the count the permute wrote exit
+  const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, shared ? a.I : 0, kBwdTileRows);
+  hipLaunchKernelGGL(k_bwd_gemm<kRowsNT>, dim3((unsigned)rtiles, (unsigned)(3 * a.I / kBN)),
+                     dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_act, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, (int)rows);
+  hipLaunchKernelGGL(k_bwd_router, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_gemm<kRowsNN>, dim3((unsigned)rtiles, (unsigned)(a.H / kBN)),
+                     dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_gemm<kWgrad>,
+                     dim3((unsigned)(a.E + 1), (unsigned)((a.I / kBM) * (a.H / kBN)), 3u),
+                     dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_router_wgrad, dim3((unsigned)a.E, (unsigned)((a.H + 255) / 256)),
+                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

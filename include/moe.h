@@ -269,6 +269,46 @@ size_t moe_aux_loss_workspace_size(int32_t T, int32_t E);
 int moe_aux_loss(int32_t T, int32_t E, const float* logits, const int32_t* counts, double* f,
                  double* P, double* loss, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- backward ---------------------------------------------------------------
+ * The layer's backward for the routing the forward chose (the training
+ * context of [Pitfalls]): the chosen experts are held fixed (the choice is
+ * piecewise constant; the expert bias only enters the choice, so it gets no
+ * gradient), the routing weights w_j = scale * s_j / (sum_k s_k + 1e-20) are
+ * differentiated through the sigmoid scores s = sigmoid(logit) of the chosen
+ * experts ([Routing §二 steps 1-3]), and y = shared(x) + sum_j w_j expert_j(x)
+ * ([Routing §四, §五]) through both projections of every SwiGLU expert.
+ * Envelope: as the forward, plus dtype MOE_BF16 and I_shared == 0 or == I
+ * (MOE_ERR_UNSUPPORTED otherwise). */
+
+/* Bytes of device workspace moe_layer_backward needs (0 on an invalid or
+ * unsupported desc).  Host only. */
+size_t moe_backward_workspace_size(const moe_desc_t* desc);
+
+/* Gradients of L = sum dy * y for the layer of `desc`:
+ *   x, weights   the forward's inputs (w_router and the expert weights are
+ *                read; expert_bias is not used)
+ *   topk_idx     (device) [T][top_k] int32: the chosen experts (the forward's
+ *                topk_idx_out), each in [0, E) (an index outside it gives
+ *                unspecified gradients for its token; every access stays
+ *                in bounds)
+ *   logits       (device) [T][E] fp32: router logits (the forward's
+ *                logits_out with MOE_F_WRITE_LOGITS)
+ *   dy           (device) [T][H] bf16: upstream gradient of y
+ *   dx           (device) [T][H] bf16 (out; must not alias x or dy)
+ *   dw_router    (device) [E][H] fp32 (out)
+ *   dw_gate, dw_up, dw_down    (device) [E][I][H] fp32 (out; zero for
+ *                experts no token chose)
+ *   dws_gate, dws_up, dws_down (device) [I_shared][H] fp32 (out), NULL iff
+ *                I_shared == 0
+ * Intermediates (g, u, r = dy W_down^T, the activation gradients) are bf16
+ * MFMA operands or fp32; accumulation is fp32; every sum runs in a fixed
+ * order (bit-reproducible).  T = 0 is a no-op. */
+int moe_layer_backward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                       const int32_t* topk_idx, const float* logits, const void* dy, void* dx,
+                       float* dw_router, float* dw_gate, float* dw_up, float* dw_down,
+                       float* dws_gate, float* dws_up, float* dws_down, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
 /* Static description of an error code. */
 const char* moe_strerror(int code);
 

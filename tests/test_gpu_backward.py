@@ -1,0 +1,130 @@
+"""GPU parity of the layer backward (moe_layer_backward, through the C ABI)
+against the oracle's fp64 backward for the same fixed routing.
+
+Data flows oracle -> GPU only: the routing (chosen experts) and the fp32
+logits the GPU backward takes are the oracle's own (its routing of the
+inputs, its fp64 logits rounded to fp32); GPU results are only compared.
+Bar: relative L2 error <= 1e-2 per gradient tensor (bf16 operands, fp32
+accumulation), the same bar as the bf16 forward; experts no token chose get
+exactly zero weight gradients; results are bit-reproducible.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_limited_top_amd import synth
+
+from gpu_helpers import DEV, L, make_layer, nb, oracle_weights, rel_l2, to_f64
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def _routing(shape, dev):
+    """The oracle's routing of the layer's inputs: idx, fp64 logits."""
+    bias = None if dev["expert_bias"] is None else nb(dev["expert_bias"])
+    idx, _, flag, l64 = oracle.route(nb(dev["x"]), nb(dev["w_router"]), bias, shape.n_group,
+                                     shape.topk_group, shape.top_k, shape.scale)
+    assert not flag.any()
+    return idx, l64
+
+
+def _dy(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape.T, shape.H, generator=g).to(torch.bfloat16)
+
+
+def _gpu_backward(shape, dev, idx, l64, dy):
+    d = L().desc_from_shape(shape)
+    weights = {k: dev[k] for k in ("w_router", "expert_bias", "w_gate", "w_up", "w_down",
+                                   "ws_gate", "ws_up", "ws_down")}
+    out = L().moe_layer_backward(d, dev["x"], weights, torch.from_numpy(idx).to(DEV),
+                                 torch.from_numpy(l64.astype(np.float32)).to(DEV), dy.to(DEV))
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_tokens(shape, dev, idx, l64, dy, gpu, tokens):
+    ref = oracle.backward_tokens(nb(dev["x"]), nb(dev["w_router"]), l64, idx, shape.scale,
+                                 dy.double().numpy(), *oracle_weights(dev), tokens=tokens)
+    got = to_f64(gpu["dx"]) if tokens is None else to_f64(gpu["dx"])[tokens]
+    r = rel_l2(got, ref["dx"])
+    say("dx rel_l2", r)
+    assert r <= TOL
+    return ref
+
+
+def _check_expert(shape, dev, idx, l64, dy, gpu, e):
+    E = shape.E
+    ref = oracle.backward_expert_weights(nb(dev["x"]), l64, idx, shape.scale, dy.double().numpy(),
+                                         e, *oracle_weights(dev))
+    names = ("dws_gate", "dws_up", "dws_down") if e >= E else ("dw_gate", "dw_up", "dw_down")
+    for name, rv in zip(names, ref):
+        gv = gpu[name] if e >= E else gpu[name][e]
+        got = gv.double().cpu().numpy()
+        if not np.any(rv):
+            np.testing.assert_array_equal(got, 0.0)
+            continue
+        r = rel_l2(got, rv)
+        say("expert", e, name, "rel_l2", r)
+        assert r <= TOL, (e, name, r)
+
+
+@pytest.mark.parametrize("T,Is", [(200, 64), (77, 0), (1, 64), (33, 64)])
+def test_backward_small_all_gradients(T, Is):
+    shape = synth.small_shape(T, H=256, I=64, I_shared=Is, bias="normal", seed=500 + T)
+    say("backward small", T, Is)
+    dev = make_layer(shape)
+    idx, l64 = _routing(shape, dev)
+    dy = _dy(shape, 7 + T)
+    gpu = _gpu_backward(shape, dev, idx, l64, dy)
+    ref = _check_tokens(shape, dev, idx, l64, dy, gpu, None)
+    # the router weight gradient from the oracle's dlogit of every token
+    dwr = oracle.router_weight_grad(nb(dev["x"]), ref["dlogit"])
+    r = rel_l2(gpu["dw_router"].double().cpu().numpy(), dwr)
+    say("dw_router rel_l2", r)
+    assert r <= TOL
+    counts = np.bincount(idx.ravel(), minlength=shape.E)
+    hot = [int(np.argmax(counts)), int(np.argsort(counts)[len(counts) // 2])]
+    cold = [int(e) for e in np.nonzero(counts == 0)[0][:1]]
+    for e in hot + cold + ([shape.E] if Is else []):
+        _check_expert(shape, dev, idx, l64, dy, gpu, e)
+    # experts no token chose: exactly zero, all of them
+    unused = counts == 0
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        assert torch.count_nonzero(gpu[name][torch.from_numpy(unused).to(DEV)]) == 0
+
+
+def test_backward_deterministic():
+    shape = synth.small_shape(300, H=256, I=64, I_shared=64, bias="normal", seed=901)
+    say("backward determinism")
+    dev = make_layer(shape)
+    idx, l64 = _routing(shape, dev)
+    dy = _dy(shape, 3)
+    a = _gpu_backward(shape, dev, idx, l64, dy)
+    b = _gpu_backward(shape, dev, idx, l64, dy)
+    for k, v in a.items():
+        if v is not None:
+            assert torch.equal(v, b[k]), k
+
+
+def test_backward_full_size_sampled():
+    """The full-size layer at 16384 tokens (with expert bias): dx on sampled
+    tokens, the weight gradients of sampled experts."""
+    shape = synth.WORKLOADS["full_t16k_bias"]
+    say("backward full_t16k_bias")
+    dev = make_layer(shape)
+    idx, l64 = _routing(shape, dev)
+    dy = _dy(shape, 11)
+    gpu = _gpu_backward(shape, dev, idx, l64, dy)
+    rng = np.random.default_rng(5)
+    tok = np.sort(rng.choice(shape.T, 48, replace=False)).astype(np.int32)
+    _check_tokens(shape, dev, idx, l64, dy, gpu, tok)
+    counts = np.bincount(idx.ravel(), minlength=shape.E)
+    for e in (int(np.argmax(counts)), int(np.argmin(counts)), 17):
+        _check_expert(shape, dev, idx, l64, dy, gpu, e)
