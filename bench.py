@@ -247,6 +247,55 @@ def bench_balance(L, d, shape, xd, weights, ws, K):
     return out
 
 
+def bench_backward(L, d, shape, xd, weights, K):
+    """The layer backward (moe_layer_backward) at this workload, for the
+    routing the forward chose and a random bf16 upstream gradient: K calls
+    captured in a HIP graph.  Algorithmic FLOP: the data and weight gradients
+    of the three projections over all R = T*(k+1) expert rows (with the shared
+    expert), 6 * 2*R*H*I; the kernels also recompute g and u (2 * 2*R*H*I more)
+    instead of keeping them from the forward.  Bytes: the fp32 weight gradients
+    written (every expert's, the shared expert's and the router's)."""
+    import torch
+    dev = xd.device
+    T, H, E, I, Is, k = shape.T, shape.H, shape.E, shape.I, shape.I_shared, shape.top_k
+    y = torch.empty(T, H, dtype=shape.torch_dtype, device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    ws = L.alloc_workspace(d, dev)
+    d.flags |= L.MOE_F_WRITE_LOGITS
+    L.moe_layer_forward(d, xd, weights, y, topk_idx_out=idx, logits_out=logits, ws=ws)
+    d.flags &= ~L.MOE_F_WRITE_LOGITS
+    g = torch.Generator(device="cpu").manual_seed(shape.seed + 77)
+    dy = torch.randn(T, H, generator=g).to(shape.torch_dtype).to(dev)
+    bws = L.backward_workspace(d, dev)
+    out = L.moe_layer_backward(d, xd, weights, idx, logits, dy, ws=bws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(K):
+            L.moe_layer_backward(d, xd, weights, idx, logits, dy, ws=bws, out=out)
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / K * 1e3
+    R = T * (k + (1 if Is else 0))
+    flops = 6 * 2 * R * H * I
+    flops_run = 8 * 2 * R * H * I
+    grad_bytes = (3 * E * I * H + (3 * Is * H) + E * H) * 4
+    tf = flops / (us * 1e-6) / 1e12
+    return {"us_per_call": round(us, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
+            "algorithmic_flops": flops, "tflops": round(tf, 2),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "executed_flops_incl_recompute": flops_run,
+            "grad_bytes_written": grad_bytes,
+            "grad_write_GBs": round(grad_bytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +306,7 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="time steps launched one by one instead of a HIP graph of K steps")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -396,6 +446,8 @@ def main():
                    "ms_per_step_eager": round(ms_step_plain, 4)},
     }
     out["balance"] = bench_balance(L, d, shape, xd, weights, ws, K)
+    if shape.dtype == "bf16" and not args.no_backward:
+        out["backward"] = bench_backward(L, d, shape, xd, weights, min(K, 10))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, x, wr, bias, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)

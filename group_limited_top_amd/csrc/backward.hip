@@ -26,11 +26,13 @@
 // terms in j order, fp32, one rounding).  Every sum has a fixed order: the
 // results are bit-reproducible.
 //
-// The GEMM tile: 64 x 64 outputs, 4 waves of 32 x 32 (2 x 2 MFMA 16x16x32
-// tiles), 32-deep K steps, operands staged in LDS (double buffer).  An operand
-// whose rows are K-contiguous in memory ("KC") is staged as [row][k] and read
-// with ds_read_b128; one stored [k][row] ("RC") is staged as is and read with
-// the gfx950 transpose read, which hands each lane 4 consecutive k of one row.
+// The GEMM tile: 64 x BN outputs (BN = 256, or 64 where a width is not a
+// multiple of 256), 4 waves each owning all 64 rows x BN / 4 columns (4 x
+// BN / 64 MFMA 16x16x32 tiles), 32-deep K steps, operands staged in LDS
+// (double buffer).  An operand whose rows are K-contiguous in memory ("KC") is
+// staged as [row][k] and read with ds_read_b128; one stored [k][row] ("RC") is
+// staged as is and read with the gfx950 transpose read, which hands each lane
+// 4 consecutive k of one row.
 #include "device.h"
 #include "expert_tiles.h"
 #include "kernels.h"
@@ -40,7 +42,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 64, kBN = 64, kBK = 32;
+constexpr int kBM = 64, kBK = 32;
 constexpr int kBT = 256;  // threads per GEMM block
 
 enum BwdGemm { kRowsNT = 0, kRowsNN = 1, kWgrad = 2 };
@@ -52,6 +54,11 @@ __device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r 
 // rows one transpose read covers over 4 chunk pairs (2 rows each).
 __device__ __forceinline__ int rc_swz(int k) { return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)); }
 __device__ __forceinline__ int rc_off(int k, int c) { return k * 128 + ((c ^ rc_swz(k)) << 4); }
+// RC staging of a 256-wide operand (rows of 512 bytes, 32 chunks): the 16 k
+// rows of one transpose read start on the same bank, so the XOR spreads them
+// over 8 chunk pairs (rows 8 q + c and 8 (q + 2) + c share one).
+__device__ __forceinline__ int rcw_swz(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+__device__ __forceinline__ int rcw_off(int k, int c) { return k * 512 + ((c ^ rcw_swz(k)) << 4); }
 
 __device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
@@ -98,43 +105,47 @@ __device__ __forceinline__ u32x4 read_kc(const uint8_t* buf, int r0, int lane) {
   const int q = lane >> 4, i = lane & 15;
   return lds16(buf + kc_off(r0 + i, q));
 }
+// RC operand of width W (64: 128-byte rows, 256: 512-byte rows)
+template <int W>
 __device__ __forceinline__ u32x4 read_rc(const uint8_t* buf, int r0, int lane) {
   // lane 4 c + m of group q points at k row 8 q + c, rows r0 + 4 m .. + 3
   const int q = lane >> 4, i = lane & 15, c = i >> 2, m = i & 3;
   const int k = 8 * q + c;
   const int col = r0 + 4 * m;
-  const uint8_t* p = buf + k * 128 + (((col >> 3) ^ rc_swz(k)) << 4) + ((col & 4) << 1);
-  const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 128);
+  const int sw = W == 64 ? rc_swz(k) : rcw_swz(k);
+  const uint8_t* p = buf + k * (2 * W) + (((col >> 3) ^ sw) << 4) + ((col & 4) << 1);
+  const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 2 * W);
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
 }  // namespace
 
-// One 64 x 64 output tile.  MODE:
+// One 64 x BN output tile.  MODE:
 //   kRowsNT: blockIdx.x = row tile, blockIdx.y = column tile over 3 I-wide
 //            segments: (x, W_g) -> g, (x, W_u) -> u, (dy, W_d) -> r; fp32 out.
 //            A rows gathered (token of each pair), B = weight rows; both KC.
 //   kRowsNN: blockIdx.x = row tile, blockIdx.y = column tile over H;
 //            K = 2 I: (d_g, W_g) then (d_u, W_u); A KC, B RC (weights
 //            [k][column]); bf16 out (per-row dx).
-//   kWgrad:  blockIdx.x = expert (E = shared), blockIdx.y = (I / 64) x (H / 64)
+//   kWgrad:  blockIdx.x = expert (E = shared), blockIdx.y = (I / 64) x (H / BN)
 //            tile, blockIdx.z = which: 0 dW_gate (d_g, x), 1 dW_up (d_u, x),
 //            2 dW_down (w a, dy); K = the expert's rows; A and B both RC
 //            (A^T: rows i of [m][i]; B: rows h of the gathered [m][h]).
-template <int MODE>
+template <int MODE, int BN>
 __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
+  constexpr int TN = BN / 64;   // MFMA column tiles per wave
+  constexpr int NB = BN / 64;   // B chunks staged per thread
   __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBM * kBK * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t sb[2][kBN * kBK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[2][BN * kBK * 2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
   const int H = a.H, I = a.I, K = a.K, E = a.E;
 
   int e = 0, row0 = 0, nrows = 0, orow = 0, n0 = 0, seg = 0, kdim = 0;
   if (MODE == kWgrad) {
     e = blockIdx.x;
-    const int it = (int)blockIdx.y / (H / kBN), ht = (int)blockIdx.y % (H / kBN);
+    const int it = (int)blockIdx.y / (H / BN), ht = (int)blockIdx.y % (H / BN);
     row0 = it * kBM;  // i range of the output
-    n0 = ht * kBN;    // h range
+    n0 = ht * BN;     // h range
     seg = blockIdx.z;
     if (e < E) {
       orow = a.offsets[e];
@@ -148,83 +159,89 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
     if ((int)blockIdx.x >= a.tile_off[E + 1]) return;  // past the real tile count
     decode_row_tile(a, blockIdx.x, e, row0, nrows, orow);
     if (MODE == kRowsNT) {
-      const int per = I / kBN;
+      const int per = I / BN;
       seg = (int)blockIdx.y / per;
-      n0 = ((int)blockIdx.y % per) * kBN;
+      n0 = ((int)blockIdx.y % per) * BN;
       kdim = H;
     } else {
-      n0 = (int)blockIdx.y * kBN;
+      n0 = (int)blockIdx.y * BN;
       kdim = 2 * I;
     }
   }
   const bool sh = e >= E;
   const size_t ebase = sh ? 0 : (size_t)e * I * H;
 
-  // staging assignment: KC: row tid / 4, chunk tid % 4; RC: k row tid / 8, chunk tid % 8
+  // staging: A one chunk per thread (KC: row tid / 4, chunk tid % 4; RC: k row
+  // tid / 8, chunk tid % 8); B NB chunks (KC: rows tid / 4 + 64 u; RC: k row
+  // tid / 8, chunks tid % 8 + 8 u)
   const int kc_r = tid >> 2, kc_c = tid & 3;
   const int rc_k = tid >> 3, rc_c = tid & 7;
-  // A (KC) row source for kRowsNT / kRowsNN
   const uint16_t* a_row = nullptr;
   const uint16_t* a_row2 = nullptr;  // kRowsNN: d_u row
-  const uint16_t* b_row = nullptr;   // kRowsNT: weight row
+  const uint16_t* b_row[NB] = {};    // kRowsNT: weight rows
   if (MODE == kRowsNT) {
     const int m = min(kc_r, nrows - 1);
     const int tok = sh ? row0 + m : a.sorted_pair[row0 + m] / K;
     a_row = (seg < 2 ? a.x : a.dy) + (size_t)tok * H;
     const uint16_t* wsrc = seg == 0 ? (sh ? a.swg : a.wg) : seg == 1 ? (sh ? a.swu : a.wu)
                                                                       : (sh ? a.swd : a.wd);
-    b_row = wsrc + ebase + (size_t)(n0 + kc_r) * H;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) b_row[u] = wsrc + ebase + (size_t)(n0 + kc_r + 64 * u) * H;
   } else if (MODE == kRowsNN) {
     const int m = min(kc_r, nrows - 1);
     a_row = a.dg + (size_t)(orow + m) * I;
     a_row2 = a.du + (size_t)(orow + m) * I;
   }
 
-  auto load = [&](int k0, u32x4& va, u32x4& vb) __attribute__((always_inline)) {
+  auto load = [&](int k0, u32x4& va, u32x4 (&vb)[NB]) __attribute__((always_inline)) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     if (MODE == kRowsNT) {
       va = ld16(a_row + k0 + 8 * kc_c);
-      vb = ld16(b_row + k0 + 8 * kc_c);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) vb[u] = ld16(b_row[u] + k0 + 8 * kc_c);
     } else if (MODE == kRowsNN) {
       const bool second = k0 >= I;
       const int kk = second ? k0 - I : k0;
       va = ld16((second ? a_row2 : a_row) + kk + 8 * kc_c);
-      const uint16_t* w = (second ? (sh ? a.swu : a.wu) : (sh ? a.swg : a.wg)) + ebase;
-      vb = ld16(w + (size_t)(kk + rc_k) * H + n0 + 8 * rc_c);
+      const uint16_t* w = (second ? (sh ? a.swu : a.wu) : (sh ? a.swg : a.wg)) + ebase +
+                          (size_t)(kk + rc_k) * H + n0 + 8 * rc_c;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) vb[u] = ld16(w + 64 * u);
     } else {
       const int m = k0 + rc_k;  // row of the expert (k of the GEMM)
       if (m < kdim) {
         const uint16_t* asrc = seg == 0 ? a.dg : seg == 1 ? a.du : a.aw;
         va = ld16(asrc + (size_t)(orow + m) * I + row0 + 8 * rc_c);
         const int tok = sh ? m : a.sorted_pair[orow + m] / K;
-        vb = ld16((seg < 2 ? a.x : a.dy) + (size_t)tok * H + n0 + 8 * rc_c);
+        const uint16_t* b = (seg < 2 ? a.x : a.dy) + (size_t)tok * H + n0 + 8 * rc_c;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) vb[u] = ld16(b + 64 * u);
       } else {
         va = z;
-        vb = z;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) vb[u] = z;
       }
     }
   };
-  auto stage = [&](int buf, const u32x4& va, const u32x4& vb) __attribute__((always_inline)) {
-    if (MODE == kRowsNT) {
-      st16(sa[buf] + kc_off(kc_r, kc_c), va);
-      st16(sb[buf] + kc_off(kc_r, kc_c), vb);
-    } else if (MODE == kRowsNN) {
-      st16(sa[buf] + kc_off(kc_r, kc_c), va);
-      st16(sb[buf] + rc_off(rc_k, rc_c), vb);
-    } else {
-      st16(sa[buf] + rc_off(rc_k, rc_c), va);
-      st16(sb[buf] + rc_off(rc_k, rc_c), vb);
+  auto stage = [&](int buf, const u32x4& va, const u32x4 (&vb)[NB]) __attribute__((always_inline)) {
+    if (MODE == kWgrad) st16(sa[buf] + rc_off(rc_k, rc_c), va);
+    else st16(sa[buf] + kc_off(kc_r, kc_c), va);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (MODE == kRowsNT) st16(sb[buf] + kc_off(kc_r + 64 * u, kc_c), vb[u]);
+      else if (BN == 64) st16(sb[buf] + rc_off(rc_k, rc_c + 8 * u), vb[u]);
+      else st16(sb[buf] + rcw_off(rc_k, rc_c + 8 * u), vb[u]);
     }
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[4][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (kdim + kBK - 1) / kBK;
-  u32x4 va, vb;
+  u32x4 va, vb[NB];
   if (nk > 0) {
     load(0, va, vb);
     stage(0, va, vb);
@@ -233,31 +250,33 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
     if (s + 1 < nk) load((s + 1) * kBK, va, vb);
-    u32x4 fa[2], fb[2];
+    u32x4 fa[4], fb[TN];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int ra = 32 * wm + 16 * t, rb = 32 * wn + 16 * t;
-      fa[t] = MODE == kWgrad ? read_rc(sa[buf], ra, lane) : read_kc(sa[buf], ra, lane);
-      fb[t] = MODE == kRowsNT ? read_kc(sb[buf], rb, lane) : read_rc(sb[buf], rb, lane);
+    for (int t = 0; t < 4; ++t)
+      fa[t] = MODE == kWgrad ? read_rc<64>(sa[buf], 16 * t, lane) : read_kc(sa[buf], 16 * t, lane);
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int rb = wv * (BN / 4) + 16 * t;
+      fb[t] = MODE == kRowsNT ? read_kc(sb[buf], rb, lane) : read_rc<BN>(sb[buf], rb, lane);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     if (s + 1 < nk) stage(buf ^ 1, va, vb);
     __syncthreads();
   }
 
-  // C[A row 16 i + 4 q + c][B row 16 j + r16] of the wave's 32 x 32
+  // C[A row 16 i + 4 q + c][B row wv * BN / 4 + 16 j + r16]
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int ar = 32 * wm + 16 * i + 4 * q + c;  // A row in the tile
-        const int bc = 32 * wn + 16 * j + r16;         // B row in the tile
+        const int ar = 16 * i + 4 * q + c;              // A row in the tile
+        const int bc = wv * (BN / 4) + 16 * j + r16;    // B row in the tile
         const float v = acc[i][j][c];
         if (MODE == kRowsNT) {
           if (ar < nrows) {
@@ -335,34 +354,94 @@ __global__ __launch_bounds__(256) void k_bwd_router(const BwdArgs a) {
   }
 }
 
-// dW_r[e][h] = sum over e's pairs (sorted order) of dlam * x[token][h].
+// dW_r[e][h] = sum over e's pairs (sorted order) of dlam * x[token][h]: one
+// block per expert, each thread 8 consecutive h (16-byte loads), the rows'
+// loads issued 8 at a time, each thread's sum in row order.
 __global__ __launch_bounds__(256) void k_bwd_router_wgrad(const BwdArgs a) {
-  const int e = blockIdx.x, h = (int)blockIdx.y * 256 + threadIdx.x;
-  if (h >= a.H) return;
+  const int e = blockIdx.x;
+  const int H = a.H, K = a.K;
   const int m0 = a.offsets[e], m1 = a.offsets[e + 1];
-  float acc = 0.0f;
-  for (int m = m0; m < m1; ++m) {
-    const int p = a.sorted_pair[m];
-    acc += a.dlam[p] * bf16_to_f32(a.x[(size_t)(p / a.K) * a.H + h]);
+  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int mb = m0; mb < m1; mb += 8) {
+      u32x4 v[8];
+      float dl[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int m = min(mb + u, m1 - 1);
+        const int p = a.sorted_pair[m];
+        dl[u] = mb + u < m1 ? a.dlam[p] : 0.0f;
+        v[u] = ld16(a.x + (size_t)(p / K) * H + h0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += dl[u] * bf16_lo(v[u][i]);
+          acc[2 * i + 1] += dl[u] * bf16_hi(v[u][i]);
+        }
+    }
+    float* out = a.dw_router + (size_t)e * H + h0;
+    *reinterpret_cast<f32x4*>(out) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
-  a.dw_router[(size_t)e * a.H + h] = acc;
 }
 
-// dx[t] = shared row + pair rows in j order + router terms in j order.
+// dx[t] = shared row + pair rows in j order + router terms in j order; each
+// thread 8 consecutive h, every row's load in flight before the sums.
 __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
+  constexpr int kMaxK = 16;
   const int t = blockIdx.x;
   const int H = a.H, K = a.K;
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float acc = a.swg ? bf16_to_f32(a.dxp[(size_t)(a.P + t) * H + h]) : 0.0f;
-    for (int j = 0; j < K; ++j) {
-      const int slot = a.pair_slot[(size_t)t * K + j];  // -1: a skipped pair
-      if (slot >= 0) acc += bf16_to_f32(a.dxp[(size_t)slot * H + h]);
+  int32_t slot[kMaxK], ex[kMaxK];
+  float dl[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;  // -1: a skipped pair
+    ex[j] = j < K ? min(max(a.idx[(size_t)t * K + j], 0), a.E - 1) : 0;
+    dl[j] = j < K ? a.dlam[(size_t)t * K + j] : 0.0f;
+  }
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
+    const u32x4 vs = a.swg ? ld16(a.dxp + (size_t)(a.P + t) * H + h0) : zero4;
+    u32x4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) v[j] = slot[j] >= 0 ? ld16(a.dxp + (size_t)slot[j] * H + h0) : zero4;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = bf16_lo(vs[i]);
+      acc[2 * i + 1] = bf16_hi(vs[i]);
     }
-    for (int j = 0; j < K; ++j) {
-      const int e = min(max(a.idx[(size_t)t * K + j], 0), a.E - 1);
-      acc += a.dlam[(size_t)t * K + j] * a.w_router[(size_t)e * H + h];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= K) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_lo(v[j][i]);
+        acc[2 * i + 1] += bf16_hi(v[j][i]);
+      }
     }
-    a.dx[(size_t)t * H + h] = (uint16_t)f32_to_bf16_bits(acc);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= K) break;
+      const float* wr = a.w_router + (size_t)ex[j] * H + h0;
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wr);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wr + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += dl[j] * w0[i];
+        acc[4 + i] += dl[j] * w1[i];
+      }
+    }
+    u32x4 pk;
+    pk.x = pack_bf16x2(acc[0], acc[1]);
+    pk.y = pack_bf16x2(acc[2], acc[3]);
+    pk.z = pack_bf16x2(acc[4], acc[5]);
+    pk.w = pack_bf16x2(acc[6], acc[7]);
+    st16(a.dx + (size_t)t * H + h0, pk);
   }
 }
 
@@ -428,17 +507,20 @@ hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
 
   // row tiles: a host upper bound; blocks past the count the permute wrote exit
   const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, shared ? a.I : 0, kBwdTileRows);
-  hipLaunchKernelGGL(k_bwd_gemm<kRowsNT>, dim3((unsigned)rtiles, (unsigned)(3 * a.I / kBN)),
-                     dim3(kBT), 0, s, a);
+  if (a.I % 256 == 0)
+    hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 256>), dim3((unsigned)rtiles, (unsigned)(3 * a.I / 256)),
+                       dim3(kBT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 64>), dim3((unsigned)rtiles, (unsigned)(3 * a.I / 64)),
+                       dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(k_bwd_act, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, (int)rows);
   hipLaunchKernelGGL(k_bwd_router, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_bwd_gemm<kRowsNN>, dim3((unsigned)rtiles, (unsigned)(a.H / kBN)),
+  hipLaunchKernelGGL((k_bwd_gemm<kRowsNN, 256>), dim3((unsigned)rtiles, (unsigned)(a.H / 256)),
                      dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(k_bwd_gemm<kWgrad>,
-                     dim3((unsigned)(a.E + 1), (unsigned)((a.I / kBM) * (a.H / kBN)), 3u),
+  hipLaunchKernelGGL((k_bwd_gemm<kWgrad, 256>),
+                     dim3((unsigned)(a.E + 1), (unsigned)((a.I / kBM) * (a.H / 256)), 3u),
                      dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(k_bwd_router_wgrad, dim3((unsigned)a.E, (unsigned)((a.H + 255) / 256)),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_router_wgrad, dim3((unsigned)a.E), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
