@@ -235,7 +235,7 @@ BwdLayout make_bwd_layout(const moe_desc_t& d) {
   L.tile_off = take((E + 2) * 4);
   L.tile_tab = take((size_t)moe::max_expert_tiles(d.T, d.top_k, d.E, d.I_shared,
                                                   moe::kBwdTileRows) * 8);
-  L.inter = take(moe::bwd_intermediate_bytes(d.T, d.top_k, d.I, d.H, d.I_shared > 0));
+  L.inter = take(moe::bwd_intermediate_bytes(d.T, d.top_k, d.E, d.I, d.H, d.I_shared > 0));
   L.total = o;
   return L;
 }

@@ -19,12 +19,20 @@
 // Steps: permute (the forward's kernels, 64-row tiles) -> k_bwd_gemm<kRowsNT>
 // (g = x W_g^T, u = x W_u^T, r = dy W_d^T, fp32) -> k_bwd_act (per row:
 // a, dL/dw, d_g, d_u, w a in bf16) -> k_bwd_router (per token: dlam) ->
-// k_bwd_gemm<kRowsNN> (per-row dx = d_g W_g + d_u W_u, bf16) ->
+// k_bwd_gemm<kRowsNN> (per-row dx = d_g W_g + d_u W_u + dlam W_r[e], bf16) ->
 // k_bwd_gemm<kWgrad> (dW_gate, dW_up, dW_down per expert, fp32, summed over
-// the expert's rows in order) -> k_bwd_router_wgrad (dW_r) -> k_bwd_combine
-// (dx per token: shared row, then the K pair rows in j order, then the router
-// terms in j order, fp32, one rounding).  Every sum has a fixed order: the
-// results are bit-reproducible.
+// the expert's rows in order) -> k_bwd_router_wgrad + k_bwd_router_reduce
+// (dW_r = dlogit^T x over token chunks, then the chunks in order) ->
+// k_bwd_combine (dx per token: shared row, then the K pair rows in j order,
+// fp32, one rounding).  Every sum has a fixed order: the results are
+// bit-reproducible.
+//
+// Block order: the row-tile GEMMs give each XCD a contiguous run of (row
+// tile, column tile) items with the column fastest, so the tiles of one expert
+// run together on one XCD and share its weight slabs and gathered rows in that
+// XCD's L2; the weight-gradient GEMM starts the shared expert's long tiles
+// first (spread over the XCDs) and then gives each XCD a contiguous run of
+// routed experts.
 //
 // The GEMM tile: 64 x BN outputs (BN = 256, or 64 where a width is not a
 // multiple of 256), 4 waves each owning all 64 rows x BN / 4 columns (4 x
@@ -33,6 +41,8 @@
 // staged as [row][k] and read with ds_read_b128; one stored [k][row] ("RC") is
 // staged as is and read with the gfx950 transpose read, which hands each lane
 // 4 consecutive k of one row.
+#include <algorithm>
+
 #include "device.h"
 #include "expert_tiles.h"
 #include "kernels.h"
@@ -62,8 +72,14 @@ __device__ __forceinline__ int rcw_off(int k, int c) { return k * 512 + ((c ^ rc
 
 __device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// Block b of a grid of n blocks (n a multiple of 8) -> work item: blocks are
+// dealt to the 8 XCDs in turn, so XCD b % 8 gets items (b % 8) n / 8 + b / 8,
+// a contiguous run.
+__device__ __forceinline__ int xcd_item(int b, int n) { return (b & 7) * (n >> 3) + (b >> 3); }
+
 struct BwdArgs {
   int T, H, E, K, I, P;  // P = T * K routed rows
+  int rtiles;            // row tiles the grids cover (a bound on the real count)
   float scale;
   const uint16_t* x;     // [T][H]
   const uint16_t* dy;    // [T][H]
@@ -142,29 +158,50 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
 
   int e = 0, row0 = 0, nrows = 0, orow = 0, n0 = 0, seg = 0, kdim = 0;
   if (MODE == kWgrad) {
-    e = blockIdx.x;
-    const int it = (int)blockIdx.y / (H / BN), ht = (int)blockIdx.y % (H / BN);
+    // items: 3 x (I / 64) x (H / BN) tiles per expert; the shared expert's
+    // first (blocks [0, ns8), dealt round the XCDs), then the routed experts'
+    const int per = 3 * (I / kBM) * (H / BN);
+    const int ns = a.swg ? per : 0, ns8 = (ns + 7) & ~7;
+    int w;
+    const int b = blockIdx.x;
+    if (b < ns8) {
+      if (b >= ns) return;
+      e = E;
+      w = b;
+    } else {
+      const int nr = E * per;
+      const int wi = xcd_item(b - ns8, (int)gridDim.x - ns8);
+      if (wi >= nr) return;
+      e = wi / per;
+      w = wi % per;
+    }
+    seg = w / (per / 3);
+    const int y = w % (per / 3);
+    const int it = y / (H / BN), ht = y % (H / BN);
     row0 = it * kBM;  // i range of the output
     n0 = ht * BN;     // h range
-    seg = blockIdx.z;
     if (e < E) {
       orow = a.offsets[e];
       kdim = a.offsets[e + 1] - orow;
     } else {
-      if (!a.swg) return;
       orow = a.P;
       kdim = a.T;
     }
   } else {
-    if ((int)blockIdx.x >= a.tile_off[E + 1]) return;  // past the real tile count
-    decode_row_tile(a, blockIdx.x, e, row0, nrows, orow);
+    // items (row tile, column tile), the column fastest
+    const int ncol = MODE == kRowsNT ? 3 * I / BN : H / BN;
+    const int w = xcd_item(blockIdx.x, gridDim.x);
+    if (w >= a.rtiles * ncol) return;
+    const int t = w / ncol, ct = w % ncol;
+    if (t >= a.tile_off[E + 1]) return;  // past the real tile count
+    decode_row_tile(a, t, e, row0, nrows, orow);
     if (MODE == kRowsNT) {
       const int per = I / BN;
-      seg = (int)blockIdx.y / per;
-      n0 = ((int)blockIdx.y % per) * BN;
+      seg = ct / per;
+      n0 = (ct % per) * BN;
       kdim = H;
     } else {
-      n0 = (int)blockIdx.y * BN;
+      n0 = ct * BN;
       kdim = 2 * I;
     }
   }
@@ -269,6 +306,21 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
 
   // C[A row 16 i + 4 q + c][B row wv * BN / 4 + 16 j + r16]
   const int q = lane >> 4, r16 = lane & 15;
+  // kRowsNN, routed rows: + dlam of the row's pair times W_r[e] (the router's
+  // share of dx), added before the one rounding to bf16
+  float rdl[4][4] = {};
+  float rw[TN] = {};
+  if (MODE == kRowsNN && !sh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int ar = 16 * i + 4 * q + c;
+        rdl[i][c] = ar < nrows ? a.dlam[a.sorted_pair[orow + ar]] : 0.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) rw[j] = a.w_router[(size_t)e * H + n0 + wv * (BN / 4) + 16 * j + r16];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -285,7 +337,8 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
           }
         } else if (MODE == kRowsNN) {
           if (ar < nrows)
-            a.dxp[(size_t)(orow + ar) * H + n0 + bc] = (uint16_t)f32_to_bf16_bits(v);
+            a.dxp[(size_t)(orow + ar) * H + n0 + bc] =
+                (uint16_t)f32_to_bf16_bits(v + rdl[i][c] * rw[j]);
         } else {
           float* out = sh ? (seg == 0 ? a.dswg : seg == 1 ? a.dswu : a.dswd)
                           : (seg == 0 ? a.dwg : seg == 1 ? a.dwu : a.dwd) + ebase;
@@ -354,55 +407,144 @@ __global__ __launch_bounds__(256) void k_bwd_router(const BwdArgs a) {
   }
 }
 
-// dW_r[e][h] = sum over e's pairs (sorted order) of dlam * x[token][h]: one
-// block per expert, each thread 8 consecutive h (16-byte loads), the rows'
-// loads issued 8 at a time, each thread's sum in row order.
-__global__ __launch_bounds__(256) void k_bwd_router_wgrad(const BwdArgs a) {
-  const int e = blockIdx.x;
-  const int H = a.H, K = a.K;
-  const int m0 = a.offsets[e], m1 = a.offsets[e + 1];
-  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
-    float acc[8];
+// dW_r = dlogit^T x, dlogit[t][e] = dlam of the pair (t, j) with idx[t][j] = e,
+// else 0, never stored: each 32-token step scatters its tokens' K values into
+// an LDS tile that is otherwise zero (the thread that owns a token slot first
+// clears the values it wrote there two steps before).  Each value v enters the
+// bf16 MFMA as two planes, hi = bf16(v) and lo = bf16(v - hi), against the
+// same x rows, so the product keeps 16 bits of v; x is bf16 already.  Tile:
+// 256 experts x 64 h, 4 waves of 64 experts x 64 h.  blockIdx.z = token chunk;
+// its sums go to part[z][e][h], summed in chunk order after.
+constexpr int kRwChunkMax = 16;
+constexpr int kRwStep = 32;  // tokens per step
+__global__ __launch_bounds__(256) void k_bwd_router_wgrad(const BwdArgs a, int chunk, float* part) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2][2][kRwStep * 512];  // [buf][hi/lo][token][expert]
+  __shared__ __attribute__((aligned(16))) uint8_t sb[2][kRwStep * 128];     // [buf][token][h]
+  __shared__ int16_t sprev[2][kRwStep][16];  // expert (- e0) each slot wrote, or -1
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, E = a.E, K = a.K;
+  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 256;
+  const int ehi = min(E - e0, 256);  // experts of this tile
+  const int t0 = blockIdx.z * chunk, t1 = min(a.T, t0 + chunk);
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  for (int i = tid; i < 2 * 2 * kRwStep * 512 / 16; i += 256) st16(&sa[0][0][0] + 16 * i, z4);
+  for (int i = tid; i < 2 * kRwStep * 16; i += 256) (&sprev[0][0][0])[i] = -1;
+  __syncthreads();
+
+  // token-slot threads (tid < 32) load the token's K (expert, dlam); every
+  // thread loads one 16-byte piece of x: token tid / 8, h chunk tid % 8
+  const int br = tid >> 3, bc = tid & 7;
+  auto load = [&](int tb, int32_t (&ix)[16], float (&dl)[16], u32x4& vb) __attribute__((always_inline)) {
+    const int t = tb + tid;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int mb = m0; mb < m1; mb += 8) {
-      u32x4 v[8];
-      float dl[8];
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = tid < kRwStep && t < t1 && j < K;
+      ix[j] = ok ? a.idx[(size_t)t * K + j] - e0 : -1;
+      dl[j] = ok ? a.dlam[(size_t)t * K + j] : 0.0f;
+    }
+    const int tx = tb + br;
+    vb = tx < t1 ? ld16(a.x + (size_t)tx * H + h0 + 8 * bc) : z4;
+  };
+  auto lds_b16 = [](uint8_t* base, int k, int el) -> uint16_t* {
+    return reinterpret_cast<uint16_t*>(base + rcw_off(k, el >> 3) + 2 * (el & 7));
+  };
+  auto stage = [&](int buf, const int32_t (&ix)[16], const float (&dl)[16], const u32x4& vb)
+      __attribute__((always_inline)) {
+    if (tid < kRwStep) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int m = min(mb + u, m1 - 1);
-        const int p = a.sorted_pair[m];
-        dl[u] = mb + u < m1 ? a.dlam[p] : 0.0f;
-        v[u] = ld16(a.x + (size_t)(p / K) * H + h0);
+      for (int j = 0; j < 16; ++j) {  // clear what this slot wrote two steps ago
+        const int el = sprev[buf][tid][j];
+        if (el >= 0) {
+          *lds_b16(sa[buf][0], tid, el) = 0;
+          *lds_b16(sa[buf][1], tid, el) = 0;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += dl[u] * bf16_lo(v[u][i]);
-          acc[2 * i + 1] += dl[u] * bf16_hi(v[u][i]);
+      for (int j = 0; j < 16; ++j) {
+        const bool in = ix[j] >= 0 && ix[j] < ehi;
+        if (in) {
+          const uint32_t hb = f32_to_bf16_bits(dl[j]);
+          const float r = dl[j] - __uint_as_float(hb << 16);
+          *lds_b16(sa[buf][0], tid, ix[j]) = (uint16_t)hb;
+          *lds_b16(sa[buf][1], tid, ix[j]) = (uint16_t)f32_to_bf16_bits(r);
         }
+        sprev[buf][tid][j] = in ? (int16_t)ix[j] : (int16_t)-1;
+      }
     }
-    float* out = a.dw_router + (size_t)e * H + h0;
-    *reinterpret_cast<f32x4*>(out) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<f32x4*>(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    st16(sb[buf] + rc_off(br, bc), vb);
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = t1 > t0 ? (t1 - t0 + kRwStep - 1) / kRwStep : 0;
+  int32_t ix[16];
+  float dl[16];
+  u32x4 vb;
+  if (nk > 0) {
+    load(t0, ix, dl, vb);
+    stage(0, ix, dl, vb);
   }
+  __syncthreads();
+  for (int st = 0; st < nk; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nk) load(t0 + kRwStep * (st + 1), ix, dl, vb);
+    u32x4 fb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = read_rc<64>(sb[buf], 16 * j, lane);
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+      u32x4 fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = read_rc<256>(sa[buf][pl], 64 * wv + 16 * i, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+    }
+    if (st + 1 < nk) stage(buf ^ 1, ix, dl, vb);
+    __syncthreads();
+  }
+  const int q = lane >> 4, r16 = lane & 15;
+  float* out = part + (size_t)blockIdx.z * E * H;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ee = e0 + 64 * wv + 16 * i + 4 * q + c;
+      if (ee < E)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[(size_t)ee * H + h0 + 16 * j + r16] = acc[i][j][c];
+    }
 }
 
-// dx[t] = shared row + pair rows in j order + router terms in j order; each
-// thread 8 consecutive h, every row's load in flight before the sums.
+// dW_r = sum of the chunks' partial sums, in chunk order; 4 values per thread.
+__global__ __launch_bounds__(256) void k_bwd_router_reduce(const BwdArgs a, int nchunk,
+                                                           const float* part) {
+  const size_t n = (size_t)a.E * a.H;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int c = 1; c < nchunk; ++c) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)c * n + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += v[k];
+  }
+  *reinterpret_cast<f32x4*>(a.dw_router + i) = acc;
+}
+
+// dx[t] = shared row + the pair rows in j order (each already holding its
+// router term); each thread 8 consecutive h, every row's load in flight
+// before the sums.
 __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
   constexpr int kMaxK = 16;
   const int t = blockIdx.x;
   const int H = a.H, K = a.K;
-  int32_t slot[kMaxK], ex[kMaxK];
-  float dl[kMaxK];
+  int32_t slot[kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;  // -1: a skipped pair
-    ex[j] = j < K ? min(max(a.idx[(size_t)t * K + j], 0), a.E - 1) : 0;
-    dl[j] = j < K ? a.dlam[(size_t)t * K + j] : 0.0f;
-  }
+  for (int j = 0; j < kMaxK; ++j) slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;  // -1: skipped
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
     const u32x4 vs = a.swg ? ld16(a.dxp + (size_t)(a.P + t) * H + h0) : zero4;
@@ -424,18 +566,6 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
         acc[2 * i + 1] += bf16_hi(v[j][i]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= K) break;
-      const float* wr = a.w_router + (size_t)ex[j] * H + h0;
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wr);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wr + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += dl[j] * w0[i];
-        acc[4 + i] += dl[j] * w1[i];
-      }
-    }
     u32x4 pk;
     pk.x = pack_bf16x2(acc[0], acc[1]);
     pk.y = pack_bf16x2(acc[2], acc[3]);
@@ -447,11 +577,15 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 
-size_t bwd_intermediate_bytes(int64_t T, int K, int I, int H, bool shared) {
+// Token chunks of the router weight gradient: up to kRwChunkMax of >= 1024
+// tokens (multiples of the step).
+static int router_chunks(int64_t T) { return (int)std::min<int64_t>(kRwChunkMax, std::max<int64_t>(1, (T + 1023) / 1024)); }
+
+size_t bwd_intermediate_bytes(int64_t T, int K, int E, int I, int H, bool shared) {
   const size_t rows = (size_t)(T * K + (shared ? T : 0));
   auto al = [](size_t b) { return (b + 255) / 256 * 256; };
   return 3 * al(rows * I * 4) + 3 * al(rows * I * 2) + 2 * al((size_t)T * K * 4) +
-         al(rows * H * 2);
+         al(rows * H * 2) + al((size_t)router_chunks(T) * E * H * 4);
 }
 
 hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
@@ -504,23 +638,31 @@ hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
   a.gw = reinterpret_cast<float*>(take((size_t)a.P * 4));
   a.dlam = reinterpret_cast<float*>(take((size_t)a.P * 4));
   a.dxp = reinterpret_cast<uint16_t*>(take((size_t)rows * a.H * 2));
+  const int nchunk = router_chunks(a.T);
+  float* rpart = reinterpret_cast<float*>(take((size_t)nchunk * a.E * a.H * 4));
+  const int chunk = (int)(((a.T + nchunk - 1) / nchunk + kRwStep - 1) / kRwStep * kRwStep);
 
   // row tiles: a host upper bound; blocks past the count the permute wrote exit
   const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, shared ? a.I : 0, kBwdTileRows);
+  a.rtiles = (int)rtiles;
+  auto grid8 = [](int64_t n) { return dim3((unsigned)((n + 7) / 8 * 8)); };
   if (a.I % 256 == 0)
-    hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 256>), dim3((unsigned)rtiles, (unsigned)(3 * a.I / 256)),
-                       dim3(kBT), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 256>), grid8(rtiles * (3 * a.I / 256)), dim3(kBT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 64>), dim3((unsigned)rtiles, (unsigned)(3 * a.I / 64)),
-                       dim3(kBT), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 64>), grid8(rtiles * (3 * a.I / 64)), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(k_bwd_act, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, (int)rows);
   hipLaunchKernelGGL(k_bwd_router, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((k_bwd_gemm<kRowsNN, 256>), dim3((unsigned)rtiles, (unsigned)(a.H / 256)),
-                     dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL((k_bwd_gemm<kWgrad, 256>),
-                     dim3((unsigned)(a.E + 1), (unsigned)((a.I / kBM) * (a.H / 256)), 3u),
-                     dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(k_bwd_router_wgrad, dim3((unsigned)a.E), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_bwd_gemm<kRowsNN, 256>), grid8(rtiles * (a.H / 256)), dim3(kBT), 0, s, a);
+  {
+    const int64_t per = 3 * (a.I / kBM) * (a.H / 256);
+    const int64_t ns8 = shared ? (per + 7) / 8 * 8 : 0;
+    const int64_t nr8 = (a.E * per + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_bwd_gemm<kWgrad, 256>), dim3((unsigned)(ns8 + nr8)), dim3(kBT), 0, s, a);
+  }
+  hipLaunchKernelGGL(k_bwd_router_wgrad, dim3((unsigned)(a.H / 64), (unsigned)((a.E + 255) / 256),
+                                              (unsigned)nchunk), dim3(256), 0, s, a, chunk, rpart);
+  hipLaunchKernelGGL(k_bwd_router_reduce, dim3((unsigned)(((size_t)a.E * a.H / 4 + 255) / 256)),
+                     dim3(256), 0, s, a, nchunk, (const float*)rpart);
   hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }

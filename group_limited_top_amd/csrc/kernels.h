@@ -118,7 +118,7 @@ struct BwdInputs {
   float *dwg, *dwu, *dwd;       // [E][I][H]
   float *dswg, *dswu, *dswd;    // [I][H] or null
 };
-size_t bwd_intermediate_bytes(int64_t T, int K, int I, int H, bool shared);
+size_t bwd_intermediate_bytes(int64_t T, int K, int E, int I, int H, bool shared);
 hipError_t launch_backward(const BwdInputs& in, hipStream_t s);
 
 // Residual + RMSNorm ----------------------------------------------------------

@@ -75,10 +75,21 @@ def _check_expert(shape, dev, idx, l64, dy, gpu, e):
         assert r <= TOL, (e, name, r)
 
 
-@pytest.mark.parametrize("T,Is", [(200, 64), (77, 0), (1, 64), (33, 64)])
-def test_backward_small_all_gradients(T, Is):
-    shape = synth.small_shape(T, H=256, I=64, I_shared=Is, bias="normal", seed=500 + T)
-    say("backward small", T, Is)
+# (T, I_shared, extra shape): token counts below and above one router-gradient
+# chunk (1024 tokens, ragged tails), no shared expert, E = 64 (a partial tile
+# of 256 experts) and 512 (two tiles), I = 320 (64-wide column tiles)
+@pytest.mark.parametrize("T,Is,kw", [
+    (200, 64, {}), (77, 0, {}), (1, 64, {}), (33, 64, {}),
+    (2500, 64, {}),
+    (300, 0, dict(E=64, n_group=4, topk_group=2, top_k=6)),
+    (1100, 64, dict(E=512, n_group=8, topk_group=4, top_k=16)),
+    (150, 320, dict(I=320)),
+])
+def test_backward_small_all_gradients(T, Is, kw):
+    kw = dict(kw)
+    I = kw.pop("I", 64)
+    shape = synth.small_shape(T, H=256, I=I, I_shared=Is, bias="normal", seed=500 + T, **kw)
+    say("backward small", T, Is, I, kw)
     dev = make_layer(shape)
     idx, l64 = _routing(shape, dev)
     dy = _dy(shape, 7 + T)
@@ -128,3 +139,15 @@ def test_backward_full_size_sampled():
     counts = np.bincount(idx.ravel(), minlength=shape.E)
     for e in (int(np.argmax(counts)), int(np.argmin(counts)), 17):
         _check_expert(shape, dev, idx, l64, dy, gpu, e)
+    # a router weight gradient row of an expert about 64 tokens chose (spread
+    # over the token chunks): only the tokens that chose it contribute, so the
+    # oracle's backward of those tokens alone gives the row exactly
+    e = int(np.argmin(np.abs(counts - 64)))
+    toks = np.nonzero((idx == e).any(axis=1))[0].astype(np.int32)
+    say("router gradient row", e, "from", len(toks), "tokens")
+    ref = oracle.backward_tokens(nb(dev["x"]), nb(dev["w_router"]), l64, idx, shape.scale,
+                                 dy.double().numpy(), *oracle_weights(dev), tokens=toks)
+    want = oracle.router_weight_grad(nb(dev["x"])[toks], ref["dlogit"])[e]
+    r = rel_l2(gpu["dw_router"][e].double().cpu().numpy(), want)
+    say("dw_router row rel_l2", r)
+    assert r <= TOL
