@@ -307,6 +307,8 @@ def main():
                     help="time steps launched one by one instead of a HIP graph of K steps")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the layer backward (prints its JSON object, not the bench line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -356,6 +358,11 @@ def main():
     y = torch.empty(shape.T, shape.H, dtype=shape.torch_dtype, device=dev)
     counts = torch.empty(shape.E, dtype=torch.int32, device=dev)
     ws = L.alloc_workspace(d, dev)
+    if args.backward_only:
+        print(json.dumps({"workload": shape.name,
+                          "backward": bench_backward(L, d, shape, xd, weights, min(args.steps, 10))}),
+              flush=True)
+        return
     stage = "gate_up"
     K, W = args.steps, args.warmup
     hev = HipEvents(2 * K)

@@ -577,9 +577,11 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 
-// Token chunks of the router weight gradient: up to kRwChunkMax of >= 1024
-// tokens (multiples of the step).
-static int router_chunks(int64_t T) { return (int)std::min<int64_t>(kRwChunkMax, std::max<int64_t>(1, (T + 1023) / 1024)); }
+// Token chunks of the router weight gradient: enough for (H / 64) x chunks to
+// fill the chip at any batch (up to kRwChunkMax chunks of >= one step).
+static int router_chunks(int64_t T) {
+  return (int)std::min<int64_t>(kRwChunkMax, std::max<int64_t>(1, (T + kRwStep - 1) / kRwStep));
+}
 
 size_t bwd_intermediate_bytes(int64_t T, int K, int E, int I, int H, bool shared) {
   const size_t rows = (size_t)(T * K + (shared ? T : 0));
