@@ -20,8 +20,9 @@
 // (g = x W_g^T, u = x W_u^T, r = dy W_d^T, fp32) -> k_bwd_act (per row:
 // a, dL/dw, d_g, d_u, w a in bf16) -> k_bwd_router (per token: dlam) ->
 // k_bwd_gemm<kRowsNN> (per-row dx = d_g W_g + d_u W_u + dlam W_r[e], bf16) ->
-// k_bwd_gemm<kWgrad> (dW_gate, dW_up, dW_down per expert, fp32, summed over
-// the expert's rows in order) -> k_bwd_router_wgrad + k_bwd_router_reduce
+// k_bwd_wgrad<2, 64> (dW_gate, dW_up) and k_bwd_wgrad<1, *> (dW_down) per
+// expert, fp32, summed over the expert's rows in order ->
+// k_bwd_router_wgrad + k_bwd_router_reduce
 // (dW_r = dlogit^T x over token chunks, then the chunks in order) ->
 // k_bwd_combine (dx per token: shared row, then the K pair rows in j order,
 // fp32, one rounding).  Every sum has a fixed order: the results are
@@ -36,11 +37,15 @@
 //
 // The GEMM tile: 64 x BN outputs (BN = 256, or 64 where a width is not a
 // multiple of 256), 4 waves each owning all 64 rows x BN / 4 columns (4 x
-// BN / 64 MFMA 16x16x32 tiles), 32-deep K steps, operands staged in LDS
+// BN / 64 MFMA 16x16x32 tiles), operands staged in LDS through registers
 // (double buffer).  An operand whose rows are K-contiguous in memory ("KC") is
 // staged as [row][k] and read with ds_read_b128; one stored [k][row] ("RC") is
 // staged as is and read with the gfx950 transpose read, which hands each lane
-// 4 consecutive k of one row.
+// 4 consecutive k of one row.  K steps are 64 deep in the g/u/r GEMM, whose
+// operands are both KC, so every staged row is a whole 128-byte line (half
+// lines halve what the load path delivers); 32 deep in the other two, whose
+// wide operand is RC with 512-byte rows (there the smaller LDS footprint,
+// more blocks per CU, measured faster).
 #include <algorithm>
 
 #include "device.h"
@@ -52,14 +57,20 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 64, kBK = 32;
+constexpr int kBM = 64;
 constexpr int kBT = 256;  // threads per GEMM block
 
-enum BwdGemm { kRowsNT = 0, kRowsNN = 1, kWgrad = 2 };
+enum BwdGemm { kRowsNT = 0, kRowsNN = 1 };
 
-// KC staging: row r (of 64), 16-byte chunk c (of 4); chunk XOR (r / 4) % 4
-// spreads 16 rows read at one chunk over all 64 banks.
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// KC staging: row r, 16-byte chunk c.  64-deep steps (8 chunks, one 128-byte
+// line a row): chunk XOR (r / 2) % 8 puts the 16 rows one read covers at one
+// logical chunk on 16 distinct 4-bank groups (row parity x 8 positions).
+// 32-deep steps (4 chunks): chunk XOR (r / 4) % 4 does the same for 64-byte
+// rows.
+template <int BK>
+__device__ __forceinline__ int kc_off(int r, int c) {
+  return BK == 64 ? r * 128 + ((c ^ ((r >> 1) & 7)) << 4) : r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
 // RC staging: k row (of 32), 16-byte chunk c (of 8); the XOR spreads the 16 k
 // rows one transpose read covers over 4 chunk pairs (2 rows each).
 __device__ __forceinline__ int rc_swz(int k) { return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)); }
@@ -116,10 +127,12 @@ __device__ __forceinline__ void decode_row_tile(const BwdArgs& a, int t, int& e,
   orow = e < a.E ? row0 : a.P + row0;  // row in the intermediates
 }
 
-// Fragment reads (lane (q, i) = (lane / 16, lane % 16)).
-__device__ __forceinline__ u32x4 read_kc(const uint8_t* buf, int r0, int lane) {
+// Fragment reads (lane (q, i) = (lane / 16, lane % 16)); KC: half h of the
+// 64-deep step is chunks 4 h .. 4 h + 3.
+template <int BK>
+__device__ __forceinline__ u32x4 read_kc(const uint8_t* buf, int r0, int h, int lane) {
   const int q = lane >> 4, i = lane & 15;
-  return lds16(buf + kc_off(r0 + i, q));
+  return lds16(buf + kc_off<BK>(r0 + i, 4 * h + q));
 }
 // RC operand of width W (64: 128-byte rows, 256: 512-byte rows)
 template <int W>
@@ -143,51 +156,20 @@ __device__ __forceinline__ u32x4 read_rc(const uint8_t* buf, int r0, int lane) {
 //   kRowsNN: blockIdx.x = row tile, blockIdx.y = column tile over H;
 //            K = 2 I: (d_g, W_g) then (d_u, W_u); A KC, B RC (weights
 //            [k][column]); bf16 out (per-row dx).
-//   kWgrad:  blockIdx.x = expert (E = shared), blockIdx.y = (I / 64) x (H / BN)
-//            tile, blockIdx.z = which: 0 dW_gate (d_g, x), 1 dW_up (d_u, x),
-//            2 dW_down (w a, dy); K = the expert's rows; A and B both RC
-//            (A^T: rows i of [m][i]; B: rows h of the gathered [m][h]).
 template <int MODE, int BN>
 __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
-  constexpr int TN = BN / 64;   // MFMA column tiles per wave
-  constexpr int NB = BN / 64;   // B chunks staged per thread
-  __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBM * kBK * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t sb[2][BN * kBK * 2];
+  constexpr int TN = BN / 64;                  // MFMA column tiles per wave
+  constexpr int BK = MODE == kRowsNT ? 64 : 32;  // K depth of a step
+  constexpr int NH = BK / 32;                  // MFMA k blocks per step
+  constexpr int NA = BK / 32;                  // A chunks staged per thread
+  constexpr int NB = BN * BK / 2048;           // B chunks staged per thread
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBM * BK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[2][BN * BK * 2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, K = a.K, E = a.E;
 
   int e = 0, row0 = 0, nrows = 0, orow = 0, n0 = 0, seg = 0, kdim = 0;
-  if (MODE == kWgrad) {
-    // items: 3 x (I / 64) x (H / BN) tiles per expert; the shared expert's
-    // first (blocks [0, ns8), dealt round the XCDs), then the routed experts'
-    const int per = 3 * (I / kBM) * (H / BN);
-    const int ns = a.swg ? per : 0, ns8 = (ns + 7) & ~7;
-    int w;
-    const int b = blockIdx.x;
-    if (b < ns8) {
-      if (b >= ns) return;
-      e = E;
-      w = b;
-    } else {
-      const int nr = E * per;
-      const int wi = xcd_item(b - ns8, (int)gridDim.x - ns8);
-      if (wi >= nr) return;
-      e = wi / per;
-      w = wi % per;
-    }
-    seg = w / (per / 3);
-    const int y = w % (per / 3);
-    const int it = y / (H / BN), ht = y % (H / BN);
-    row0 = it * kBM;  // i range of the output
-    n0 = ht * BN;     // h range
-    if (e < E) {
-      orow = a.offsets[e];
-      kdim = a.offsets[e + 1] - orow;
-    } else {
-      orow = a.P;
-      kdim = a.T;
-    }
-  } else {
+  {
     // items (row tile, column tile), the column fastest
     const int ncol = MODE == kRowsNT ? 3 * I / BN : H / BN;
     const int w = xcd_item(blockIdx.x, gridDim.x);
@@ -208,66 +190,70 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
   const bool sh = e >= E;
   const size_t ebase = sh ? 0 : (size_t)e * I * H;
 
-  // staging: A one chunk per thread (KC: row tid / 4, chunk tid % 4; RC: k row
-  // tid / 8, chunk tid % 8); B NB chunks (KC: rows tid / 4 + 64 u; RC: k row
-  // tid / 8, chunks tid % 8 + 8 u)
-  const int kc_r = tid >> 2, kc_c = tid & 3;
-  const int rc_k = tid >> 3, rc_c = tid & 7;
-  const uint16_t* a_row = nullptr;
-  const uint16_t* a_row2 = nullptr;  // kRowsNN: d_u row
-  const uint16_t* b_row[NB] = {};    // kRowsNT: weight rows
+  // Staging (chunk = 16 bytes):
+  //   KC (CA = BK / 8 chunks a row): A rows tid / CA + (256 / CA) u, chunk
+  //     tid % CA; kRowsNT B rows likewise.
+  //   kRowsNN B (RC, BK k rows of BN / 8 chunks): k row n / (BN / 8), chunk
+  //     n % (BN / 8) for n = tid + 256 u.
+  constexpr int CA = BK / 8, RS = 256 / CA;
+  const int kr = tid / CA, kc = tid % CA;
+  const uint16_t* a_row[NA] = {};
+  const uint16_t* a_row2[NA] = {};  // kRowsNN: d_u rows
+  const uint16_t* b_row[NB] = {};   // kRowsNT: weight rows
   if (MODE == kRowsNT) {
-    const int m = min(kc_r, nrows - 1);
-    const int tok = sh ? row0 + m : a.sorted_pair[row0 + m] / K;
-    a_row = (seg < 2 ? a.x : a.dy) + (size_t)tok * H;
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int m = min(kr + RS * u, nrows - 1);
+      const int tok = sh ? row0 + m : a.sorted_pair[row0 + m] / K;
+      a_row[u] = (seg < 2 ? a.x : a.dy) + (size_t)tok * H + 8 * kc;
+    }
     const uint16_t* wsrc = seg == 0 ? (sh ? a.swg : a.wg) : seg == 1 ? (sh ? a.swu : a.wu)
                                                                       : (sh ? a.swd : a.wd);
 #pragma unroll
-    for (int u = 0; u < NB; ++u) b_row[u] = wsrc + ebase + (size_t)(n0 + kc_r + 64 * u) * H;
+    for (int u = 0; u < NB; ++u) b_row[u] = wsrc + ebase + (size_t)(n0 + kr + RS * u) * H + 8 * kc;
   } else if (MODE == kRowsNN) {
-    const int m = min(kc_r, nrows - 1);
-    a_row = a.dg + (size_t)(orow + m) * I;
-    a_row2 = a.du + (size_t)(orow + m) * I;
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int m = min(kr + RS * u, nrows - 1);
+      a_row[u] = a.dg + (size_t)(orow + m) * I + 8 * kc;
+      a_row2[u] = a.du + (size_t)(orow + m) * I + 8 * kc;
+    }
   }
+  constexpr int CPR = BN / 8;  // kRowsNN B: chunks per k row
 
-  auto load = [&](int k0, u32x4& va, u32x4 (&vb)[NB]) __attribute__((always_inline)) {
+  auto load = [&](int k0, u32x4 (&va)[NA], u32x4 (&vb)[NB]) __attribute__((always_inline)) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     if (MODE == kRowsNT) {
-      va = ld16(a_row + k0 + 8 * kc_c);
 #pragma unroll
-      for (int u = 0; u < NB; ++u) vb[u] = ld16(b_row[u] + k0 + 8 * kc_c);
+      for (int u = 0; u < NA; ++u) va[u] = ld16(a_row[u] + k0);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) vb[u] = ld16(b_row[u] + k0);
     } else if (MODE == kRowsNN) {
       const bool second = k0 >= I;
       const int kk = second ? k0 - I : k0;
-      va = ld16((second ? a_row2 : a_row) + kk + 8 * kc_c);
+#pragma unroll
+      for (int u = 0; u < NA; ++u) va[u] = ld16((second ? a_row2[u] : a_row[u]) + kk);
       const uint16_t* w = (second ? (sh ? a.swu : a.wu) : (sh ? a.swg : a.wg)) + ebase +
-                          (size_t)(kk + rc_k) * H + n0 + 8 * rc_c;
+                          (size_t)kk * H + n0;
 #pragma unroll
-      for (int u = 0; u < NB; ++u) vb[u] = ld16(w + 64 * u);
-    } else {
-      const int m = k0 + rc_k;  // row of the expert (k of the GEMM)
-      if (m < kdim) {
-        const uint16_t* asrc = seg == 0 ? a.dg : seg == 1 ? a.du : a.aw;
-        va = ld16(asrc + (size_t)(orow + m) * I + row0 + 8 * rc_c);
-        const int tok = sh ? m : a.sorted_pair[orow + m] / K;
-        const uint16_t* b = (seg < 2 ? a.x : a.dy) + (size_t)tok * H + n0 + 8 * rc_c;
-#pragma unroll
-        for (int u = 0; u < NB; ++u) vb[u] = ld16(b + 64 * u);
-      } else {
-        va = z;
-#pragma unroll
-        for (int u = 0; u < NB; ++u) vb[u] = z;
+      for (int u = 0; u < NB; ++u) {
+        const int n = tid + 256 * u;
+        vb[u] = ld16(w + (size_t)(n / CPR) * H + 8 * (n % CPR));
       }
     }
   };
-  auto stage = [&](int buf, const u32x4& va, const u32x4 (&vb)[NB]) __attribute__((always_inline)) {
-    if (MODE == kWgrad) st16(sa[buf] + rc_off(rc_k, rc_c), va);
-    else st16(sa[buf] + kc_off(kc_r, kc_c), va);
+  auto stage = [&](int buf, const u32x4 (&va)[NA], const u32x4 (&vb)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u) st16(sa[buf] + kc_off<BK>(kr + RS * u, kc), va[u]);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      if (MODE == kRowsNT) st16(sb[buf] + kc_off(kc_r + 64 * u, kc_c), vb[u]);
-      else if (BN == 64) st16(sb[buf] + rc_off(rc_k, rc_c + 8 * u), vb[u]);
-      else st16(sb[buf] + rcw_off(rc_k, rc_c + 8 * u), vb[u]);
+      if (MODE == kRowsNT) {
+        st16(sb[buf] + kc_off<BK>(kr + RS * u, kc), vb[u]);
+      } else {
+        const int n = tid + 256 * u;
+        if (BN == 64) st16(sb[buf] + rc_off(n / CPR, n % CPR), vb[u]);
+        else st16(sb[buf] + rcw_off(n / CPR, n % CPR), vb[u]);
+      }
     }
   };
 
@@ -277,8 +263,8 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (kdim + kBK - 1) / kBK;
-  u32x4 va, vb[NB];
+  const int nk = (kdim + BK - 1) / BK;
+  u32x4 va[NA], vb[NB];
   if (nk > 0) {
     load(0, va, vb);
     stage(0, va, vb);
@@ -286,20 +272,24 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
   __syncthreads();
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nk) load((s + 1) * kBK, va, vb);
-    u32x4 fa[4], fb[TN];
+    if (s + 1 < nk) load((s + 1) * BK, va, vb);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      fa[t] = MODE == kWgrad ? read_rc<64>(sa[buf], 16 * t, lane) : read_kc(sa[buf], 16 * t, lane);
+    for (int h = 0; h < NH; ++h) {
+      u32x4 fa[4], fb[TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const int rb = wv * (BN / 4) + 16 * t;
-      fb[t] = MODE == kRowsNT ? read_kc(sb[buf], rb, lane) : read_rc<BN>(sb[buf], rb, lane);
+      for (int t = 0; t < 4; ++t)
+        fa[t] = read_kc<BK>(sa[buf], 16 * t, h, lane);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int rb = wv * (BN / 4) + 16 * t;
+        fb[t] = MODE == kRowsNT ? read_kc<BK>(sb[buf], rb, h, lane)
+                                : read_rc<BN>(sb[buf] + h * 32 * 2 * BN, rb, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     if (s + 1 < nk) stage(buf ^ 1, va, vb);
     __syncthreads();
   }
@@ -345,6 +335,146 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
           out[(size_t)(row0 + ar) * H + n0 + bc] = v;
         }
       }
+}
+
+// Weight gradients, K = the expert's rows (32 a step).  NSEG = 2: dW_gate and
+// dW_up from d_g, d_u against the same x rows (x staged once for both), AW =
+// 64 features; NSEG = 1: dW_down from w a against dy rows, AW = 128 (or 64).
+// Tile: NSEG x AW features x 256 h; wave w owns h 64 w .. + 63 of every
+// feature.  The MFMA takes the h side as its row operand, so each lane ends
+// with 4 consecutive h of one feature: one 16-byte store.  All operands are
+// RC (rows of the expert), staged as is and read with the transpose read.
+// Items: the shared expert's first (its K is T; blocks dealt round the
+// XCDs), then the routed experts', each XCD a contiguous run of them.
+template <int NSEG, int AW>
+__global__ __launch_bounds__(256) void k_bwd_wgrad(const BwdArgs a) {
+  constexpr int NT = AW / 16;               // feature tiles per segment
+  constexpr int NAC = AW / 64;              // A chunks staged per thread per segment
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2][NSEG][32 * AW * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[2][32 * 512];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, I = a.I, K = a.K, E = a.E;
+  const int nh = H / 256, per = (I / AW) * nh;
+  const int ns = a.swg ? per : 0, ns8 = (ns + 7) & ~7;
+  int e, w;
+  const int b = blockIdx.x;
+  if (b < ns8) {
+    if (b >= ns) return;
+    e = E;
+    w = b;
+  } else {
+    const int wi = xcd_item(b - ns8, (int)gridDim.x - ns8);
+    if (wi >= E * per) return;
+    e = wi / per;
+    w = wi % per;
+  }
+  const int i0 = (w / nh) * AW, h0 = (w % nh) * 256;
+  const bool sh = e >= E;
+  const int orow = sh ? a.P : a.offsets[e];
+  const int kdim = sh ? a.T : a.offsets[e + 1] - orow;
+  const uint16_t* asrc[NSEG];
+  if (NSEG == 2) {
+    asrc[0] = a.dg;
+    asrc[NSEG - 1] = a.du;
+  } else {
+    asrc[0] = a.aw;
+  }
+  const uint16_t* bsrc = NSEG == 2 ? a.x : a.dy;
+
+  // staging: A k row tid / (AW / 8) (+ 256 / (AW / 8) u), chunk tid % (AW / 8);
+  // B k row tid / 8, chunks tid % 8 + 8 u (one gathered row per thread)
+  constexpr int ACR = AW / 8;
+  const int br = tid >> 3, bc = tid & 7;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  auto tok_of = [&](int m) -> int {
+    return m < kdim ? (sh ? m : a.sorted_pair[orow + m] / K) : -1;
+  };
+  auto load = [&](int k0, int tok, u32x4 (&va)[NSEG][NAC], u32x4 (&vb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+#pragma unroll
+      for (int u = 0; u < NAC; ++u) {
+        const int n = tid + 256 * u;
+        const int m = k0 + n / ACR;
+        va[sg][u] = m < kdim ? ld16(asrc[sg] + (size_t)(orow + m) * I + i0 + 8 * (n % ACR)) : z4;
+      }
+    const uint16_t* bp = bsrc + (size_t)(tok < 0 ? 0 : tok) * H + h0 + 8 * bc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vb[u] = tok >= 0 ? ld16(bp + 64 * u) : z4;
+  };
+  auto stage = [&](int buf, const u32x4 (&va)[NSEG][NAC], const u32x4 (&vb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+#pragma unroll
+      for (int u = 0; u < NAC; ++u) {
+        const int n = tid + 256 * u;
+        if (AW == 64) st16(sa[buf][sg] + rc_off(n / ACR, n % ACR), va[sg][u]);
+        else st16(sa[buf][sg] + (n / ACR) * 256 + (((n % ACR) ^ rcw_swz(n / ACR)) << 4), va[sg][u]);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st16(sb[buf] + rcw_off(br, bc + 8 * u), vb[u]);
+  };
+
+  f32x4 acc[NSEG * NT][4];
+#pragma unroll
+  for (int i = 0; i < NSEG * NT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = (kdim + 31) / 32;
+  u32x4 va[NSEG][NAC], vb[4];
+  int tok_n = tok_of(br);        // token of this thread's B row, next step to load
+  if (nk > 0) {
+    load(0, tok_n, va, vb);
+    stage(0, va, vb);
+    tok_n = tok_of(32 + br);
+  }
+  __syncthreads();
+  for (int st = 0; st < nk; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nk) {
+      load(32 * (st + 1), tok_n, va, vb);
+      tok_n = tok_of(32 * (st + 2) + br);  // one step ahead of its rows
+    }
+    u32x4 fh[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fh[j] = read_rc<256>(sb[buf], 64 * wv + 16 * j, lane);
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        u32x4 fi;
+        if (AW == 64) {
+          fi = read_rc<64>(sa[buf][sg], 16 * t, lane);
+        } else {
+          // 256-byte rows: the same transpose read with the 16-chunk swizzle
+          const int q = lane >> 4, i = lane & 15, c = i >> 2, m = i & 3;
+          const int k = 8 * q + c;
+          const int col = 16 * t + 4 * m;
+          const uint8_t* p = sa[buf][sg] + k * 256 + (((col >> 3) ^ rcw_swz(k)) << 4) + ((col & 4) << 1);
+          const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 256);
+          fi = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[sg * NT + t][j] = mfma16x16x32(fh[j], fi, acc[sg * NT + t][j]);
+      }
+    if (st + 1 < nk) stage(buf ^ 1, va, vb);
+    __syncthreads();
+  }
+  // lane: feature i0 + 16 t + r16, h h0 + 64 wv + 16 j + 4 q .. + 3
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    float* out;
+    if (NSEG == 2) out = sg == 0 ? (sh ? a.dswg : a.dwg) : (sh ? a.dswu : a.dwu);
+    else out = sh ? a.dswd : a.dwd;
+    if (!sh) out += (size_t)e * I * H;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(out + (size_t)(i0 + 16 * t + r16) * H + h0 + 64 * wv + 16 * j + 4 * q) =
+            acc[sg * NT + t][j];
+  }
 }
 
 // Per row (one wave): a = silu(g) u, dL/dw = <a, r> (routed rows), d_a = w r,
@@ -656,10 +786,16 @@ hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
   hipLaunchKernelGGL(k_bwd_router, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_bwd_gemm<kRowsNN, 256>), grid8(rtiles * (a.H / 256)), dim3(kBT), 0, s, a);
   {
-    const int64_t per = 3 * (a.I / kBM) * (a.H / 256);
-    const int64_t ns8 = shared ? (per + 7) / 8 * 8 : 0;
-    const int64_t nr8 = (a.E * per + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_bwd_gemm<kWgrad, 256>), dim3((unsigned)(ns8 + nr8)), dim3(kBT), 0, s, a);
+    auto grid_w = [&](int aw) {
+      const int64_t per = (a.I / aw) * (a.H / 256);
+      const int64_t ns8 = shared ? (per + 7) / 8 * 8 : 0;
+      return dim3((unsigned)(ns8 + (a.E * per + 7) / 8 * 8));
+    };
+    hipLaunchKernelGGL((k_bwd_wgrad<2, 64>), grid_w(64), dim3(256), 0, s, a);
+    if (a.I % 128 == 0)
+      hipLaunchKernelGGL((k_bwd_wgrad<1, 128>), grid_w(128), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_wgrad<1, 64>), grid_w(64), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(k_bwd_router_wgrad, dim3((unsigned)(a.H / 64), (unsigned)((a.E + 255) / 256),
                                               (unsigned)nchunk), dim3(256), 0, s, a, chunk, rpart);
