@@ -157,7 +157,7 @@ __device__ __forceinline__ u32x4 read_rc(const uint8_t* buf, int r0, int lane) {
 //            K = 2 I: (d_g, W_g) then (d_u, W_u); A KC, B RC (weights
 //            [k][column]); bf16 out (per-row dx).
 template <int MODE, int BN>
-__global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
+__global__ __launch_bounds__(kBT, 2) void k_bwd_gemm(const BwdArgs a) {
   constexpr int TN = BN / 64;                  // MFMA column tiles per wave
   constexpr int BK = MODE == kRowsNT ? 64 : 32;  // K depth of a step
   constexpr int NH = BK / 32;                  // MFMA k blocks per step
@@ -222,7 +222,6 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
   constexpr int CPR = BN / 8;  // kRowsNN B: chunks per k row
 
   auto load = [&](int k0, u32x4 (&va)[NA], u32x4 (&vb)[NB]) __attribute__((always_inline)) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
     if (MODE == kRowsNT) {
 #pragma unroll
       for (int u = 0; u < NA; ++u) va[u] = ld16(a_row[u] + k0);
@@ -264,15 +263,7 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (kdim + BK - 1) / BK;
-  u32x4 va[NA], vb[NB];
-  if (nk > 0) {
-    load(0, va, vb);
-    stage(0, va, vb);
-  }
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load((s + 1) * BK, va, vb);
+  auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       u32x4 fa[4], fb[TN];
@@ -290,8 +281,29 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     }
-    if (s + 1 < nk) stage(buf ^ 1, va, vb);
+  };
+  // Loads run two steps ahead of the MFMAs and LDS stores one: at step s the
+  // register set staged at the end of step s - 1 takes step s + 2's loads,
+  // and the set loaded at step s - 1 is staged for step s + 1.  The step count
+  // is even (H / 64 and 2 I / 32) and nothing in the loop is conditional
+  // (loads past the last step repeat it, stores past it go to the free
+  // buffer), so the compiler's load waits count only the older set.
+  u32x4 va0[NA], vb0[NB], va1[NA], vb1[NB];
+  auto step = [&](int s, u32x4 (&fa)[NA], u32x4 (&fb)[NB], const u32x4 (&la)[NA],
+                  const u32x4 (&lb)[NB]) __attribute__((always_inline)) {
+    load(min(s + 2, nk - 1) * BK, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    compute(s & 1);
+    stage((s + 1) & 1, la, lb);
     __syncthreads();
+  };
+  load(0, va0, vb0);
+  stage(0, va0, vb0);
+  load(min(1, nk - 1) * BK, va1, vb1);
+  __syncthreads();
+  for (int s = 0; s < nk; s += 2) {
+    step(s, va0, vb0, va1, vb1);
+    step(s + 1, va1, vb1, va0, vb0);
   }
 
   // C[A row 16 i + 4 q + c][B row wv * BN / 4 + 16 j + r16]
@@ -347,7 +359,7 @@ __global__ __launch_bounds__(kBT) void k_bwd_gemm(const BwdArgs a) {
 // Items: the shared expert's first (its K is T; blocks dealt round the
 // XCDs), then the routed experts', each XCD a contiguous run of them.
 template <int NSEG, int AW>
-__global__ __launch_bounds__(256) void k_bwd_wgrad(const BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_bwd_wgrad(const BwdArgs a) {
   constexpr int NT = AW / 16;               // feature tiles per segment
   constexpr int NAC = AW / 64;              // A chunks staged per thread per segment
   __shared__ __attribute__((aligned(16))) uint8_t sa[2][NSEG][32 * AW * 2];
@@ -386,8 +398,21 @@ __global__ __launch_bounds__(256) void k_bwd_wgrad(const BwdArgs a) {
   constexpr int ACR = AW / 8;
   const int br = tid >> 3, bc = tid & 7;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  auto tok_of = [&](int m) -> int {
-    return m < kdim ? (sh ? m : a.sorted_pair[orow + m] / K) : -1;
+  // Rows past the expert's end are loaded from its last row (always a valid
+  // address, no branch) and zeroed when staged.  The token of this lane's B
+  // row k0 + br: wave w's rows are k0 + 8 w .. + 7, read with scalar loads
+  // (they never wait on the data loads' counter) and picked per lane.
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* const sp_p = uniform_ptr(a.sorted_pair + (sh ? 0 : orow));
+  auto tok_of = [&](int k0) -> int {
+    if (sh) return min(k0 + br, kdim - 1);
+    int v = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int32_t sv = sload(sp_p + min(k0 + 8 * wu + j, kdim - 1));
+      v = (lane >> 3) == j ? sv : v;
+    }
+    return v / K;
   };
   auto load = [&](int k0, int tok, u32x4 (&va)[NSEG][NAC], u32x4 (&vb)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -395,24 +420,27 @@ __global__ __launch_bounds__(256) void k_bwd_wgrad(const BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < NAC; ++u) {
         const int n = tid + 256 * u;
-        const int m = k0 + n / ACR;
-        va[sg][u] = m < kdim ? ld16(asrc[sg] + (size_t)(orow + m) * I + i0 + 8 * (n % ACR)) : z4;
+        const int m = min(k0 + n / ACR, kdim - 1);
+        va[sg][u] = ld16(asrc[sg] + (size_t)(orow + m) * I + i0 + 8 * (n % ACR));
       }
-    const uint16_t* bp = bsrc + (size_t)(tok < 0 ? 0 : tok) * H + h0 + 8 * bc;
+    const uint16_t* bp = bsrc + (size_t)tok * H + h0 + 8 * bc;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vb[u] = tok >= 0 ? ld16(bp + 64 * u) : z4;
+    for (int u = 0; u < 4; ++u) vb[u] = ld16(bp + 64 * u);
   };
-  auto stage = [&](int buf, const u32x4 (&va)[NSEG][NAC], const u32x4 (&vb)[4]) __attribute__((always_inline)) {
+  auto stage = [&](int buf, int k0, const u32x4 (&va)[NSEG][NAC], const u32x4 (&vb)[4])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int sg = 0; sg < NSEG; ++sg)
 #pragma unroll
       for (int u = 0; u < NAC; ++u) {
         const int n = tid + 256 * u;
-        if (AW == 64) st16(sa[buf][sg] + rc_off(n / ACR, n % ACR), va[sg][u]);
-        else st16(sa[buf][sg] + (n / ACR) * 256 + (((n % ACR) ^ rcw_swz(n / ACR)) << 4), va[sg][u]);
+        const u32x4 v = k0 + n / ACR < kdim ? va[sg][u] : z4;
+        if (AW == 64) st16(sa[buf][sg] + rc_off(n / ACR, n % ACR), v);
+        else st16(sa[buf][sg] + (n / ACR) * 256 + (((n % ACR) ^ rcw_swz(n / ACR)) << 4), v);
       }
+    const bool bok = k0 + br < kdim;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) st16(sb[buf] + rcw_off(br, bc + 8 * u), vb[u]);
+    for (int u = 0; u < 4; ++u) st16(sb[buf] + rcw_off(br, bc + 8 * u), bok ? vb[u] : z4);
   };
 
   f32x4 acc[NSEG * NT][4];
@@ -420,21 +448,23 @@ __global__ __launch_bounds__(256) void k_bwd_wgrad(const BwdArgs a) {
   for (int i = 0; i < NSEG * NT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = (kdim + 31) / 32;
-  u32x4 va[NSEG][NAC], vb[4];
-  int tok_n = tok_of(br);        // token of this thread's B row, next step to load
-  if (nk > 0) {
-    load(0, tok_n, va, vb);
-    stage(0, va, vb);
-    tok_n = tok_of(32 + br);
-  }
-  __syncthreads();
-  for (int st = 0; st < nk; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nk) {
-      load(32 * (st + 1), tok_n, va, vb);
-      tok_n = tok_of(32 * (st + 2) + br);  // one step ahead of its rows
+  const int nk = (kdim + 31) / 32;  // steps of 32 rows
+  if (nk == 0) {                    // no rows: the gradients are zero
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) {
+      float* out = NSEG == 2 ? (sg == 0 ? a.dwg : a.dwu) : a.dwd;
+      out += (size_t)e * I * H;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(out + (size_t)(i0 + 16 * t + r16) * H + h0 + 64 * wv + 16 * j + 4 * q) =
+              f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    return;
+  }
+  auto compute = [&](int buf) __attribute__((always_inline)) {
     u32x4 fh[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) fh[j] = read_rc<256>(sb[buf], 64 * wv + 16 * j, lane);
@@ -457,9 +487,30 @@ __global__ __launch_bounds__(256) void k_bwd_wgrad(const BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[sg * NT + t][j] = mfma16x16x32(fh[j], fi, acc[sg * NT + t][j]);
       }
-    if (st + 1 < nk) stage(buf ^ 1, va, vb);
+  };
+  // Loads two steps ahead of the MFMAs, LDS stores one, nothing in the loop
+  // conditional (as in k_bwd_gemm); the token of a gathered row is read a
+  // step before the row itself.
+  u32x4 va0[NSEG][NAC], vb0[4], va1[NSEG][NAC], vb1[4];
+  auto step = [&](int st, int& tok_n, u32x4 (&fa)[NSEG][NAC], u32x4 (&fb)[4],
+                  const u32x4 (&la)[NSEG][NAC], const u32x4 (&lb)[4]) __attribute__((always_inline)) {
+    load(32 * (st + 2), tok_n, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    compute(st & 1);
+    tok_n = tok_of(32 * (st + 3));
+    stage((st + 1) & 1, 32 * (st + 1), la, lb);
     __syncthreads();
+  };
+  load(0, tok_of(0), va0, vb0);
+  stage(0, 0, va0, vb0);
+  load(32, tok_of(32), va1, vb1);
+  int tok_n = tok_of(64);
+  __syncthreads();
+  for (int st = 0; st + 1 < nk; st += 2) {
+    step(st, tok_n, va0, vb0, va1, vb1);
+    step(st + 1, tok_n, va1, vb1, va0, vb0);
   }
+  if (nk & 1) compute((nk - 1) & 1);  // staged by the step before (or the prologue)
   // lane: feature i0 + 16 t + r16, h h0 + 64 wv + 16 j + 4 q .. + 3
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
