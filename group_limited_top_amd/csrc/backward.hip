@@ -276,10 +276,12 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_gemm(const BwdArgs a) {
         fb[t] = MODE == kRowsNT ? read_kc<BK>(sb[buf], rb, h, lane)
                                 : read_rc<BN>(sb[buf] + h * 32 * 2 * BN, rb, lane);
       }
+      // the column side as the MFMA's row operand: each lane ends with 4
+      // consecutive output columns of one row (one wide store)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(fb[j], fa[i], acc[i][j]);
     }
   };
   // Loads run two steps ahead of the MFMAs and LDS stores one: at step s the
@@ -306,47 +308,40 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_gemm(const BwdArgs a) {
     step(s + 1, va1, vb1, va0, vb0);
   }
 
-  // C[A row 16 i + 4 q + c][B row wv * BN / 4 + 16 j + r16]
+  // acc[i][j][c] = C[A row 16 i + r16][B row wv * BN / 4 + 16 j + 4 q + c]
   const int q = lane >> 4, r16 = lane & 15;
   // kRowsNN, routed rows: + dlam of the row's pair times W_r[e] (the router's
   // share of dx), added before the one rounding to bf16
-  float rdl[4][4] = {};
-  float rw[TN] = {};
+  float rdl[4] = {};
+  f32x4 rw[TN] = {};
   if (MODE == kRowsNN && !sh) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int ar = 16 * i + 4 * q + c;
-        rdl[i][c] = ar < nrows ? a.dlam[a.sorted_pair[orow + ar]] : 0.0f;
-      }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) rw[j] = a.w_router[(size_t)e * H + n0 + wv * (BN / 4) + 16 * j + r16];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int ar = 16 * i + r16;
+      rdl[i] = ar < nrows ? a.dlam[a.sorted_pair[orow + ar]] : 0.0f;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
+      rw[j] = *reinterpret_cast<const f32x4*>(a.w_router + (size_t)e * H + n0 + wv * (BN / 4) + 16 * j + 4 * q);
+  }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int ar = 16 * i + 4 * q + c;              // A row in the tile
-        const int bc = wv * (BN / 4) + 16 * j + r16;    // B row in the tile
-        const float v = acc[i][j][c];
-        if (MODE == kRowsNT) {
-          if (ar < nrows) {
-            float* out = seg == 0 ? a.g : seg == 1 ? a.u : a.r;
-            out[(size_t)(orow + ar) * I + n0 + bc] = v;
-          }
-        } else if (MODE == kRowsNN) {
-          if (ar < nrows)
-            a.dxp[(size_t)(orow + ar) * H + n0 + bc] =
-                (uint16_t)f32_to_bf16_bits(v + rdl[i][c] * rw[j]);
-        } else {
-          float* out = sh ? (seg == 0 ? a.dswg : seg == 1 ? a.dswu : a.dswd)
-                          : (seg == 0 ? a.dwg : seg == 1 ? a.dwu : a.dwd) + ebase;
-          out[(size_t)(row0 + ar) * H + n0 + bc] = v;
-        }
+  for (int i = 0; i < 4; ++i) {
+    const int ar = 16 * i + r16;  // A row in the tile
+    if (ar >= nrows) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int bc = wv * (BN / 4) + 16 * j + 4 * q;  // first of 4 B rows in the tile
+      if (MODE == kRowsNT) {
+        float* out = seg == 0 ? a.g : seg == 1 ? a.u : a.r;
+        *reinterpret_cast<f32x4*>(out + (size_t)(orow + ar) * I + n0 + bc) = acc[i][j];
+      } else {
+        u32x2 pk;
+        pk.x = pack_bf16x2(acc[i][j][0] + rdl[i] * rw[j][0], acc[i][j][1] + rdl[i] * rw[j][1]);
+        pk.y = pack_bf16x2(acc[i][j][2] + rdl[i] * rw[j][2], acc[i][j][3] + rdl[i] * rw[j][3]);
+        *reinterpret_cast<u32x2*>(a.dxp + (size_t)(orow + ar) * H + n0 + bc) = pk;
       }
+    }
+  }
 }
 
 // Weight gradients, K = the expert's rows (32 a step).  NSEG = 2: dW_gate and
@@ -496,7 +491,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_wgrad(const BwdArgs a) {
                   const u32x4 (&la)[NSEG][NAC], const u32x4 (&lb)[4]) __attribute__((always_inline)) {
     load(32 * (st + 2), tok_n, fa, fb);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(st & 1);
+    // the compute of a step past the end (an odd count) is skipped; it issues
+    // no memory loads, so the loads' waits are the same either way
+    if (st < nk) compute(st & 1);
     tok_n = tok_of(32 * (st + 3));
     stage((st + 1) & 1, 32 * (st + 1), la, lb);
     __syncthreads();
@@ -506,11 +503,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_wgrad(const BwdArgs a) {
   load(32, tok_of(32), va1, vb1);
   int tok_n = tok_of(64);
   __syncthreads();
-  for (int st = 0; st + 1 < nk; st += 2) {
+  for (int st = 0; st < nk; st += 2) {
     step(st, tok_n, va0, vb0, va1, vb1);
     step(st + 1, tok_n, va1, vb1, va0, vb0);
   }
-  if (nk & 1) compute((nk - 1) & 1);  // staged by the step before (or the prologue)
   // lane: feature i0 + 16 t + r16, h h0 + 64 wv + 16 j + 4 q .. + 3
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -543,27 +539,57 @@ __global__ __launch_bounds__(256) void k_bwd_act(const BwdArgs a, int nrows_tota
   if (row < a.P) {
     p = a.sorted_pair[row];
     const int t = p / K, j = p - (p / K) * K;
-    // the token's routing weights from its chosen experts' logits, j order
+    // the token's routing weights from its chosen experts' logits (every
+    // load issued before the sums), summed in j order
+    int ix[16];
+    float lg[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ix[k] = min(max(a.idx[(size_t)t * K + min(k, K - 1)], 0), E - 1);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lg[k] = a.logits[(size_t)t * E + ix[k]];
     float S = 0.0f, sj = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      const float s = sigm(a.logits[(size_t)t * E + min(max(a.idx[(size_t)t * K + k], 0), E - 1)]);
-      S += s;
-      if (k == j) sj = s;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k >= K) continue;
+      const float sk = sigm(lg[k]);
+      S += sk;
+      sj = k == j ? sk : sj;
     }
     w = a.scale * (sj / (S + 1e-20f));
   }
   const size_t base = (size_t)row * I;
   float dot = 0.0f;
-  for (int i = lane; i < I; i += 64) {
-    const float g = a.g[base + i], u = a.u[base + i], r = a.r[base + i];
-    const float sg = sigm(g);
-    const float silu = g * sg;
-    const float act = silu * u;
-    dot += act * r;
-    const float da = w * r;
-    a.dg[base + i] = (uint16_t)f32_to_bf16_bits(da * u * (sg * (1.0f + g * (1.0f - sg))));
-    a.du[base + i] = (uint16_t)f32_to_bf16_bits(da * silu);
-    a.aw[base + i] = (uint16_t)f32_to_bf16_bits(w * act);
+  for (int i0 = 8 * lane; i0 < I; i0 += 512) {  // 8 consecutive features a lane
+    f32x4 gv[2], uv[2], rv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      gv[h] = *reinterpret_cast<const f32x4*>(a.g + base + i0 + 4 * h);
+      uv[h] = *reinterpret_cast<const f32x4*>(a.u + base + i0 + 4 * h);
+      rv[h] = *reinterpret_cast<const f32x4*>(a.r + base + i0 + 4 * h);
+    }
+    float dg[8], du[8], aw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float g = gv[k >> 2][k & 3], u = uv[k >> 2][k & 3], r = rv[k >> 2][k & 3];
+      const float sg = sigm(g);
+      const float silu = g * sg;
+      const float act = silu * u;
+      dot += act * r;
+      const float da = w * r;
+      dg[k] = da * u * (sg * (1.0f + g * (1.0f - sg)));
+      du[k] = da * silu;
+      aw[k] = w * act;
+    }
+    u32x4 pg, pu, pa;
+    pg.x = pack_bf16x2(dg[0], dg[1]); pg.y = pack_bf16x2(dg[2], dg[3]);
+    pg.z = pack_bf16x2(dg[4], dg[5]); pg.w = pack_bf16x2(dg[6], dg[7]);
+    pu.x = pack_bf16x2(du[0], du[1]); pu.y = pack_bf16x2(du[2], du[3]);
+    pu.z = pack_bf16x2(du[4], du[5]); pu.w = pack_bf16x2(du[6], du[7]);
+    pa.x = pack_bf16x2(aw[0], aw[1]); pa.y = pack_bf16x2(aw[2], aw[3]);
+    pa.z = pack_bf16x2(aw[4], aw[5]); pa.w = pack_bf16x2(aw[6], aw[7]);
+    st16(a.dg + base + i0, pg);
+    st16(a.du + base + i0, pu);
+    st16(a.aw + base + i0, pa);
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) dot += __shfl_xor(dot, o, 64);
@@ -738,9 +764,11 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
       acc[2 * i] = bf16_lo(vs[i]);
       acc[2 * i + 1] = bf16_hi(vs[i]);
     }
+    // (skip, not break: a break lets the compiler sink each row's load into
+    // its iteration, one load in flight at a time)
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-      if (j >= K) break;
+      if (slot[j] < 0) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += bf16_lo(v[j][i]);
