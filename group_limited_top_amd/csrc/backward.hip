@@ -29,11 +29,11 @@
 // bit-reproducible.
 //
 // Block order: the row-tile GEMMs give each XCD a contiguous run of (row
-// tile, column tile) items with the column fastest, so the tiles of one expert
-// run together on one XCD and share its weight slabs and gathered rows in that
-// XCD's L2; the weight-gradient GEMM starts the shared expert's long tiles
-// first (spread over the XCDs) and then gives each XCD a contiguous run of
-// routed experts.
+// tile, column tile) items, expert by expert and column-major within one, so
+// the tiles of one expert run together on one XCD and those sharing a weight
+// slab start together (they read it once into that XCD's L2); the
+// weight-gradient kernels start the shared expert's long tiles first (spread
+// over the XCDs) and then give each XCD a contiguous run of routed experts.
 //
 // The GEMM tile: 64 x BN outputs (BN = 256, or 64 where a width is not a
 // multiple of 256), 4 waves each owning all 64 rows x BN / 4 columns (4 x
@@ -170,12 +170,17 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_gemm(const BwdArgs a) {
 
   int e = 0, row0 = 0, nrows = 0, orow = 0, n0 = 0, seg = 0, kdim = 0;
   {
-    // items (row tile, column tile), the column fastest
+    // items expert by expert; within an expert column-major, so the row
+    // tiles that share a weight slab are consecutive: they start together and
+    // read the slab's K window from L2 (row-major, they started up to most of
+    // a tile's run apart and the expert's slabs did not fit the XCD's L2)
     const int ncol = MODE == kRowsNT ? 3 * I / BN : H / BN;
     const int w = xcd_item(blockIdx.x, gridDim.x);
-    if (w >= a.rtiles * ncol) return;
-    const int t = w / ncol, ct = w % ncol;
-    if (t >= a.tile_off[E + 1]) return;  // past the real tile count
+    if (w >= a.tile_off[E + 1] * ncol) return;  // past the real tile count
+    const int g = upper_bound_i32(a.tile_off, E + 2, w / ncol) - 1;
+    const int t0 = a.tile_off[g], nt = a.tile_off[g + 1] - t0;
+    const int local = w - t0 * ncol;
+    const int t = t0 + local % nt, ct = local / nt;
     decode_row_tile(a, t, e, row0, nrows, orow);
     if (MODE == kRowsNT) {
       const int per = I / BN;
