@@ -6,6 +6,7 @@
 #include <math.h>
 #include <string.h>
 
+#include "backward.h"
 #include "kernels.h"
 
 namespace {

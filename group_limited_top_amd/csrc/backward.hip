@@ -48,6 +48,7 @@
 // more blocks per CU, measured faster).
 #include <algorithm>
 
+#include "backward.h"
 #include "device.h"
 #include "expert_tiles.h"
 #include "kernels.h"

@@ -100,27 +100,6 @@ size_t aux_workspace_bytes(int T, int E);
 hipError_t launch_aux_loss(const float* logits, const int32_t* counts, double* f, double* P,
                            double* loss, double* part, int T, int E, hipStream_t s);
 
-// Backward --------------------------------------------------------------------
-constexpr int kBwdTileRows = 64;  // row tiles of the backward's grouped GEMMs
-struct BwdInputs {
-  int T, H, E, K, I;  // I: routed = shared intermediate size (or no shared expert)
-  float scale;
-  const uint16_t *x, *dy;       // [T][H] bf16
-  const float* logits;          // [T][E]
-  const int32_t* idx;           // [T][K]
-  const float* w_router;        // [E][H]
-  const uint16_t *wg, *wu, *wd;    // [E][I][H]
-  const uint16_t *swg, *swu, *swd; // [I][H] or null
-  const int32_t *offsets, *sorted_pair, *pair_slot, *tile_off, *tile_tab;  // permute output
-  void* scratch;                // bwd_intermediate_bytes
-  uint16_t* dx;                 // [T][H]
-  float* dw_router;             // [E][H]
-  float *dwg, *dwu, *dwd;       // [E][I][H]
-  float *dswg, *dswu, *dswd;    // [I][H] or null
-};
-size_t bwd_intermediate_bytes(int64_t T, int K, int E, int I, int H, bool shared);
-hipError_t launch_backward(const BwdInputs& in, hipStream_t s);
-
 // Residual + RMSNorm ----------------------------------------------------------
 hipError_t launch_residual_rmsnorm(bool bf16, const void* x_in, const void* y, void* x_out,
                                    void* r_out, int T, int H, float eps, hipStream_t s);
