@@ -162,6 +162,96 @@ def write_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
     print(json.dumps({workload: entry}, indent=1))
 
 
+def measure_peaks():
+    """What this GPU reaches on a pure streaming read of 4 GiB (global -> LDS
+    loads) and on a loop of register-operand bf16 MFMAs (libmoe_probe,
+    include/moe_probe.h): the best of a few launches each, timed with HIP
+    events."""
+    import ctypes
+    import torch
+    so = os.path.join(ROOT, "group_limited_top_amd", "libmoe_probe.so")
+    lib = ctypes.CDLL(so)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    blocks, iters = 1024, 256
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+
+    def read():
+        rc = lib.moe_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
+                                       ctypes.c_void_p(sink.data_ptr()), 4096, stream)
+        if rc != 0:
+            raise RuntimeError(f"moe_probe_stream_read failed ({rc})")
+
+    def mfma():
+        rc = lib.moe_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
+        if rc != 0:
+            raise RuntimeError(f"moe_probe_mfma_bf16 failed ({rc})")
+
+    gbs = nbytes / (best(read, 5) * 1e-3) / 1e9
+    tflops = blocks * 4 * iters * 8 * 16384 / (best(mfma, 3) * 1e-3) / 1e12
+    del buf
+    return {"hbm_read_GBs": round(gbs, 1), "bf16_mfma_TFLOPs": round(tflops, 1),
+            "how": "libmoe_probe: global->LDS DMA reads of 4 GiB (4 KiB a wave a round), best of 5; "
+                   "8 independent v_mfma_f32_16x16x32_bf16 chains per wave, 4096 waves, best of 3"}
+
+
+def gpu_clocks():
+    """sclk / memory clock / power read with rocm-smi right after the timed
+    region (a child process; None where the tool or a field is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(r.stdout).values()))
+    except Exception:
+        return None
+    keep = {}
+    for k, v in card.items():
+        kl = k.lower()
+        if "sclk" in kl or "mclk" in kl or "power" in kl:
+            keep[k] = v
+    return keep or None
+
+
+def verify_logits_run(L, d, shape, xd, weights, ws, y_timed, counts_timed):
+    """A forward that also writes the router logits must give the timed run's
+    y and counts bit for bit (and the same choices as a plain forward)."""
+    import torch
+    dev = xd.device
+    T, E, k = shape.T, shape.E, shape.top_k
+    y0 = torch.empty_like(y_timed)
+    y1 = torch.empty_like(y_timed)
+    i0 = torch.empty(T, k, dtype=torch.int32, device=dev)
+    i1 = torch.empty(T, k, dtype=torch.int32, device=dev)
+    c1 = torch.empty_like(counts_timed)
+    lg = torch.empty(T, E, dtype=torch.float32, device=dev)
+    L.moe_layer_forward(d, xd, weights, y0, topk_idx_out=i0, ws=ws)
+    d.flags |= L.MOE_F_WRITE_LOGITS
+    L.moe_layer_forward(d, xd, weights, y1, topk_idx_out=i1, logits_out=lg, counts_out=c1, ws=ws)
+    d.flags &= ~L.MOE_F_WRITE_LOGITS
+    torch.cuda.synchronize()
+    same = (torch.equal(y1.view(torch.int16), y_timed.view(torch.int16))
+            and torch.equal(y0.view(torch.int16), y_timed.view(torch.int16))
+            and torch.equal(i0, i1) and torch.equal(c1, counts_timed))
+    return {"logits_run_bit_identical": bool(same),
+            "what": "y, counts of a forward writing logits vs the timed run's; idx vs a plain forward"}
+
+
 def cpu_baseline(shape, x, wr, bias, w, max_tokens):
     """The oracle as it stands: routing for every token, experts + combine for
     the first `max_tokens` tokens; throughput scaled to tokens/s."""
@@ -187,8 +277,27 @@ def cpu_baseline(shape, x, wr, bias, w, max_tokens):
     per_token = t_route / shape.T + t_exp / n
     sample = (f"routing of all {shape.T} tokens ({t_route:.2f} s) + experts and combine of "
               f"{n} tokens ({t_exp:.2f} s), scaled per token")
+    # the same sample on one thread
+    t0 = time.perf_counter()
+    oracle.route(xb, wrb, b, shape.n_group, shape.topk_group, shape.top_k, shape.scale, 1)
+    t_route1 = time.perf_counter() - t0
+    n1 = min(n, 64)
+    t0 = time.perf_counter()
+    oracle.experts(xb, idx, tw, *ow, tokens=tok[:n1], nthreads=1)
+    t_exp1 = time.perf_counter() - t0
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample,
+            "value_1thread": round(1.0 / (t_route1 / shape.T + t_exp1 / n1), 2),
+            "sample_1thread": f"routing of all {shape.T} tokens + experts and combine of {n1} tokens",
+            "cpu_model": cpu, "nproc": os.cpu_count()}
 
 
 def bench_balance(L, d, shape, xd, weights, ws, K):
@@ -307,6 +416,8 @@ def main():
                     help="time steps launched one by one instead of a HIP graph of K steps")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the streaming-read and MFMA rates of this GPU")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the layer backward (prints its JSON object, not the bench line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -414,6 +525,8 @@ def main():
         torch.cuda.synchronize()
         ms_step_graph = g0.elapsed_time(g1) / K
     assert L.moe_status(ws) == 0
+    clocks = gpu_clocks()
+    verification = verify_logits_run(L, d, shape, xd, weights, ws, y, counts)
 
     work = algorithmic_work(shape, counts.cpu().numpy())
     ms_value = ms_step_graph if ms_step_graph is not None else ms_step
@@ -426,6 +539,11 @@ def main():
         achieved = work["k_gate_up"] / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    peaks = None if args.no_peaks else measure_peaks()
+    if peaks:
+        mp = peaks["bf16_mfma_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_read_GBs"]
+        roof["measured_peak"] = mp
+        roof["frac_vs_measured"] = round(roof["achieved"] / mp, 4)
     kname = L.moe_stage_kernel(d, stage)
     roof["traffic"] = measured_traffic(shape.name, kname)
     roof.update(kernel=kname,
@@ -442,6 +560,9 @@ def main():
                    "top_k": shape.top_k, "moe_intermediate": shape.I,
                    "shared_intermediate": shape.I_shared, "expert_bias": shape.bias},
         "roofline": roof,
+        "peaks_measured": peaks,
+        "clocks_after_timed_region": clocks,
+        "verification": verification,
         "layer": {"algorithmic_bytes": work["layer"], "hbm_GBs": round(layer_hbm, 1),
                   "hbm_frac": round(layer_hbm / HBM_PEAK_GBS, 4), "tflops": round(layer_tflops, 2),
                   "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),

@@ -19,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SO = os.path.join(PKG, "libmoe.so")
+PROBE_SO = os.path.join(PKG, "libmoe_probe.so")  # measurement kernels (bench.py only)
 ARCH = "gfx950"
 
 
@@ -29,8 +30,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe)")
 
 
-def command(out: str = SO) -> list[str]:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def command(out: str = SO, srcs: list[str] | None = None) -> list[str]:
+    if srcs is None:
+        srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -38,19 +40,25 @@ def command(out: str = SO) -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = SO + ".tmp"
-    cmd = command(tmp)
+def _compile(out: str, srcs: list[str] | None, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = command(tmp, srcs)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"libmoe build failed:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"{os.path.basename(out)} build failed:\n{r.stdout}\n{r.stderr}")
     noise = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, SO)
-    return SO
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libmoe.so and the measurement library libmoe_probe.so."""
+    _compile(PROBE_SO, [os.path.join(PKG, "probe", "probe.hip")], verbose)
+    return _compile(SO, None, verbose)
 
 
 if __name__ == "__main__":

@@ -175,3 +175,30 @@ def test_balance_entry_points_reject_bad_arguments(L):
     assert lib.moe_aux_loss(16384, 256, fake, fake, fake, fake, fake, fake, n - 1, None) == -3
     assert lib.moe_aux_loss(16384, 256, fake, fake, fake, fake, fake, None, n, None) == -3
     assert lib.moe_aux_loss(16384, 256, fake, fake, odd, fake, fake, fake, n, None) == -4
+
+
+# --------------------------------------------------------------------------- measurement probes
+
+PROBE_HEADER = os.path.join(ROOT, "include", "moe_probe.h")
+
+
+def test_probe_library_exports_its_header():
+    """libmoe_probe.so (the streaming-read and MFMA-loop kernels bench.py
+    measures this GPU with) exports what include/moe_probe.h declares and
+    rejects bad arguments on the host."""
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_probe_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["moe_probe_mfma_bf16", "moe_probe_stream_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "group_limited_top_amd", "libmoe_probe.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    bad = 1  # hipErrorInvalidValue
+    lib.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    assert lib.moe_probe_stream_read(None, 4096, None, 16, None) == bad
+    assert lib.moe_probe_stream_read(16, 4000, 16, 16, None) == bad      # not whole 4 KiB pieces
+    assert lib.moe_probe_stream_read(8, 4096, 16, 16, None) == bad       # misaligned
+    assert lib.moe_probe_stream_read(16, 4096, 16, 0, None) == bad       # no blocks
+    lib.moe_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.moe_probe_mfma_bf16(None, 4, 4, None) == bad
+    assert lib.moe_probe_mfma_bf16(16, 0, 4, None) == bad
