@@ -177,6 +177,50 @@ def test_balance_entry_points_reject_bad_arguments(L):
     assert lib.moe_aux_loss(16384, 256, fake, fake, odd, fake, fake, fake, n, None) == -4
 
 
+def test_backward_entry_points_reject_bad_arguments(L):
+    """moe_backward_workspace_size / moe_layer_backward: the backward's
+    envelope (bf16, shared expert as wide as the routed ones), T = 0 as a
+    no-op, and argument errors found on the host before any launch."""
+    lib = L.LIB
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: errors come first
+    odd = ctypes.c_void_p(0x100008)
+    d = full_desc(L)
+    n = lib.moe_backward_workspace_size(ctypes.byref(d))
+    assert n > 0 and n % 256 == 0
+    # grows with the batch; unsupported descs give 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(full_desc(L, T=1024))) > n
+    f32 = full_desc(L)
+    f32.dtype = L.MOE_F32
+    assert lib.moe_backward_workspace_size(ctypes.byref(f32)) == 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(full_desc(L, I_shared=128))) == 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(full_desc(L, I_shared=0))) > 0
+
+    def call(desc, W, x=fake, idx=fake, lg=fake, dy=fake, dx=ctypes.c_void_p(0x200000),
+             shared=True, ws=fake, nbytes=1 << 40):
+        s = fake if shared else None
+        return lib.moe_layer_backward(ctypes.byref(desc), x, ctypes.byref(W) if W else None, idx, lg,
+                                      dy, dx, fake, fake, fake, fake, s, s, s, ws, nbytes, None)
+
+    W = L.MoeWeights(fake, None, fake, fake, fake, fake, fake, fake)
+    # T = 0: nothing to do, nothing checked past the descriptor
+    d0 = full_desc(L, T=0)
+    assert lib.moe_layer_backward(ctypes.byref(d0), None, None, None, None, None, None, None, None,
+                                  None, None, None, None, None, None, 0, None) == 0
+    assert call(f32, W) == -2                                # fp32 layer: unsupported
+    assert call(full_desc(L, I_shared=128), W) == -2         # narrower shared expert
+    assert call(d, None) == -1                               # no weights
+    assert call(d, W, x=None) == -1
+    assert call(d, W, lg=None) == -1
+    assert call(d, W, dx=fake) == -1                         # dx aliasing x
+    assert call(d, W, shared=False) == -1                    # shared gradients missing
+    assert call(full_desc(L, I_shared=0), L.MoeWeights(fake, None, fake, fake, fake, None, None, None),
+                shared=True) == -1                           # ... or given without a shared expert
+    assert call(d, W, dy=odd) == -4
+    assert call(d, W, nbytes=n - 1) == -3
+    assert call(d, W, ws=None) == -3
+    assert call(d, W, ws=odd) == -4
+
+
 # --------------------------------------------------------------------------- measurement probes
 
 PROBE_HEADER = os.path.join(ROOT, "include", "moe_probe.h")

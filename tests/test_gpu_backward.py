@@ -151,3 +151,31 @@ def test_backward_full_size_sampled():
     r = rel_l2(gpu["dw_router"][e].double().cpu().numpy(), want)
     say("dw_router row rel_l2", r)
     assert r <= TOL
+
+
+def test_backward_skewed_routing():
+    """Every token picks expert 0 and seven of experts 1..32: expert 0's rows
+    are all the tokens (many row tiles of one expert, long weight-gradient
+    sums), experts past 32 get none.  Any routing is a valid point of the
+    fixed-routing backward, so the choice is given, not computed."""
+    T = 1500
+    shape = synth.small_shape(T, H=256, I=64, I_shared=64, bias="normal", seed=77)
+    say("backward skewed routing", T)
+    dev = make_layer(shape)
+    rng = np.random.default_rng(3)
+    idx = np.empty((T, shape.top_k), np.int32)
+    idx[:, 0] = 0
+    for t in range(T):
+        idx[t, 1:] = 1 + rng.choice(32, shape.top_k - 1, replace=False)
+    l64 = oracle.logits_any(nb(dev["x"]), nb(dev["w_router"]))
+    dy = _dy(shape, 19)
+    gpu = _gpu_backward(shape, dev, idx, l64, dy)
+    ref = _check_tokens(shape, dev, idx, l64, dy, gpu, None)
+    dwr = oracle.router_weight_grad(nb(dev["x"]), ref["dlogit"])
+    r = rel_l2(gpu["dw_router"].double().cpu().numpy(), dwr)
+    say("dw_router rel_l2", r)
+    assert r <= TOL
+    for e in (0, 5, 32, 100, shape.E):
+        _check_expert(shape, dev, idx, l64, dy, gpu, e)
+    assert torch.count_nonzero(gpu["dw_gate"][33:]) == 0
+    assert torch.count_nonzero(gpu["dw_down"][33:]) == 0
