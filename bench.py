@@ -252,6 +252,73 @@ def verify_logits_run(L, d, shape, xd, weights, ws, y_timed, counts_timed):
             "what": "y, counts of a forward writing logits vs the timed run's; idx vs a plain forward"}
 
 
+def bench_stack(L, shape, K, W):
+    """The residual stack workload (independent layers, x <- RN(x + layer(
+    RN(RMSNorm(x))))): K passes through all layers captured in one HIP graph,
+    each pass starting from the same x (a 2-byte-per-element device copy
+    inside the graph, ~0.5% of a pass).  Per-layer fractions use the layer's
+    algorithmic FLOP and bytes with the counts of each layer's routing."""
+    import torch
+    dev = "cuda"
+    nl = shape.layers
+    layers = []
+    for l in range(nl):
+        _, wr, bias = synth_router(shape, l)
+        w = synth_weights(shape, l)
+        layers.append(dict(w, w_router=wr.to(dev), expert_bias=None if bias is None else bias.to(dev)))
+    x0 = synth_router(shape, 0)[0].to(dev)
+    d = L.desc_from_shape(shape)
+    ws = L.alloc_workspace(d, dev)
+    x = torch.empty_like(x0)
+    counts = torch.empty(nl, shape.E, dtype=torch.int32, device=dev)
+    for _ in range(max(W, 1)):
+        x.copy_(x0)
+        L.moe_stack_forward(d, x, layers, ws, counts_out=counts)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(K):
+            x.copy_(x0)
+            L.moe_stack_forward(d, x, layers, ws)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    c = counts.cpu().numpy()
+    work = [algorithmic_work(shape, c[l]) for l in range(nl)]
+    flops = sum(wk["flops_layer"] for wk in work)
+    nbytes = sum(wk["layer"] for wk in work)
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": METRIC, "value": round(shape.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": shape.dtype, "data": "synthetic",
+            "config": {"workload": shape.name, "tokens": shape.T, "layers": nl, "hidden": shape.H,
+                       "experts": shape.E, "top_k": shape.top_k, "moe_intermediate": shape.I,
+                       "shared_intermediate": shape.I_shared},
+            "step": f"one pass through {nl} layers (RMSNorm, MoE layer, residual each)",
+            "ms_per_layer": round(ms / nl, 4),
+            "layer_avg": {"tflops": round(tf, 2), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                          "hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "algorithmic_flops_per_layer": round(flops / nl),
+                          "algorithmic_bytes_per_layer": round(nbytes / nl)}}
+
+
+def synth_router(shape, layer):
+    from group_limited_top_amd import synth
+    return synth.router_inputs(shape, layer)
+
+
+def synth_weights(shape, layer):
+    from group_limited_top_amd import synth
+    return synth.expert_weights(shape, device="cuda", layer=layer)
+
+
 def cpu_baseline(shape, x, wr, bias, w, max_tokens):
     """The oracle as it stands: routing for every token, experts + combine for
     the first `max_tokens` tokens; throughput scaled to tokens/s."""
@@ -454,7 +521,9 @@ def main():
 
     shape = synth.WORKLOADS[args.workload]
     if shape.layers != 1:
-        raise SystemExit("bench.py times single-layer workloads")
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_stack(L, shape, min(args.steps, 10), min(args.warmup, 2))), flush=True)
+        return
     dev = "cuda"
     torch.cuda.set_device(0)
     x, wr, bias = synth.router_inputs(shape)

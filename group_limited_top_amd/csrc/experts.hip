@@ -544,6 +544,8 @@ hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTim
 // ----------------------------------------------------------------------------
 // residual + RMSNorm (for stacking layers; gamma = 1), one block per row
 // ----------------------------------------------------------------------------
+// Rows too wide to keep in registers (bf16 beyond 32768 features): two passes,
+// the second reading x_out back.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_residual_rmsnorm(const void* x_in, const void* y,
                                                            void* x_out, void* r_out, int H,
@@ -587,14 +589,102 @@ __global__ __launch_bounds__(256) void k_residual_rmsnorm(const void* x_in, cons
   }
 }
 
+// The same with the row in registers: thread i holds 16-byte chunks i, i + 256,
+// ... (NC of them), so x_out is written once and never read back; sums: each
+// thread's elements in order, then the wave (butterfly), then the 4 waves in
+// order.
+template <bool BF16, int NC>
+__global__ __launch_bounds__(256) void k_residual_rmsnorm_reg(const void* x_in, const void* y,
+                                                               void* x_out, void* r_out, int H,
+                                                               float eps) {
+  constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int nch = H / EPC;
+  const size_t row = (size_t)t * nch;  // chunk index of the row's start
+  const u32x4* xi = reinterpret_cast<const u32x4*>(x_in) + row;
+  const u32x4* yi = y ? reinterpret_cast<const u32x4*>(y) + row : nullptr;
+  u32x4* xo = reinterpret_cast<u32x4*>(x_out) + row;
+  u32x4* ro = reinterpret_cast<u32x4*>(r_out) + row;
+  float v[NC][EPC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = tid + 256 * j;
+    if (c >= nch) continue;
+    const u32x4 a = xi[c];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const u32x4 b = yi ? yi[c] : zero4;
+    u32x4 out;
+    if (BF16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float lo = bf16_lo(a[k]), hi = bf16_hi(a[k]);
+        if (yi) {
+          lo = lo + bf16_lo(b[k]);
+          hi = hi + bf16_hi(b[k]);
+        }
+        out[k] = pack_bf16x2(lo, hi);
+        v[j][2 * k] = bf16_lo(out[k]);
+        v[j][2 * k + 1] = bf16_hi(out[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float f = __uint_as_float(a[k]);
+        if (yi) f = f + __uint_as_float(b[k]);
+        v[j][k] = f;
+        out[k] = __float_as_uint(f);
+      }
+    }
+    xo[c] = out;
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) ss = __builtin_fmaf(v[j][k], v[j][k], ss);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = tid + 256 * j;
+    if (c >= nch) continue;
+    u32x4 out;
+    if (BF16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[k] = pack_bf16x2(v[j][2 * k] * inv, v[j][2 * k + 1] * inv);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[k] = __float_as_uint(v[j][k] * inv);
+    }
+    ro[c] = out;
+  }
+}
+
 hipError_t launch_residual_rmsnorm(bool bf16, const void* x_in, const void* y, void* x_out,
                                    void* r_out, int T, int H, float eps, hipStream_t s) {
-  if (bf16)
-    hipLaunchKernelGGL(k_residual_rmsnorm<true>, dim3((unsigned)T), dim3(256), 0, s, x_in, y, x_out,
-                       r_out, H, eps);
-  else
-    hipLaunchKernelGGL(k_residual_rmsnorm<false>, dim3((unsigned)T), dim3(256), 0, s, x_in, y,
-                       x_out, r_out, H, eps);
+  const int nch = H / (bf16 ? 8 : 4);
+  const int per = (nch + 255) / 256;  // chunks per thread
+  const dim3 g((unsigned)T), b(256);
+#define MOE_RMS(B, N) hipLaunchKernelGGL((k_residual_rmsnorm_reg<B, N>), g, b, 0, s, x_in, y, x_out, r_out, H, eps)
+  if (bf16) {
+    if (per <= 1) MOE_RMS(true, 1);
+    else if (per <= 2) MOE_RMS(true, 2);
+    else if (per <= 4) MOE_RMS(true, 4);
+    else if (per <= 8) MOE_RMS(true, 8);
+    else if (per <= 16) MOE_RMS(true, 16);
+    else hipLaunchKernelGGL(k_residual_rmsnorm<true>, g, b, 0, s, x_in, y, x_out, r_out, H, eps);
+  } else {
+    if (per <= 1) MOE_RMS(false, 1);
+    else if (per <= 2) MOE_RMS(false, 2);
+    else if (per <= 4) MOE_RMS(false, 4);
+    else if (per <= 8) MOE_RMS(false, 8);
+    else if (per <= 16) MOE_RMS(false, 16);
+    else hipLaunchKernelGGL(k_residual_rmsnorm<false>, g, b, 0, s, x_in, y, x_out, r_out, H, eps);
+  }
+#undef MOE_RMS
   return hipGetLastError();
 }
 

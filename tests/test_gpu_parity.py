@@ -496,37 +496,48 @@ def test_layer_skew_t64k_sampled():
 
 # --------------------------------------------------------------------------- residual + RMSNorm
 
-def test_residual_rmsnorm():
-    """x_out = RN_bf16(x + y) (at most a rare 1-ulp double-rounding difference
-    from the fp32 add) and r_out = RN_bf16(RMSNorm(x_out)) within one bf16 ulp of
-    the fp64 oracle."""
-    say("residual rmsnorm")
+@pytest.mark.parametrize("dtype,H", [("bf16", 2048), ("bf16", 256), ("bf16", 6144),
+                                     ("bf16", 40960), ("fp32", 512), ("fp32", 16384)])
+def test_residual_rmsnorm(dtype, H):
+    """x_out = RN(x + y) (bf16: at most a rare 1-ulp double-rounding
+    difference from the fp32 add; fp32: exact) and r_out = RN(RMSNorm(x_out))
+    within one ulp-scale of the fp64 oracle.  Widths cover one to sixteen
+    16-byte chunks per thread, a partial last round, and rows too wide for
+    registers (the two-pass kernel)."""
+    say("residual rmsnorm", dtype, H)
     Lb = L()
-    T, H = 37, 2048
-    g = torch.Generator().manual_seed(5)
-    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
-    y = (0.3 * torch.randn(T, H, generator=g)).to(torch.bfloat16)
-    d = Lb.make_desc(T, H)
-    xo = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    T = 37
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(5 + H)
+    x = torch.randn(T, H, generator=g).to(tdt)
+    y = (0.3 * torch.randn(T, H, generator=g)).to(tdt)
+    d = Lb.make_desc(T, H, dtype=dtype)
+    xo = torch.empty(T, H, dtype=tdt, device=DEV)
     ro = torch.empty_like(xo)
     Lb.moe_residual_rmsnorm(d, x.to(DEV), y.to(DEV), xo, ro, 1e-6)
     torch.cuda.synchronize()
-    ref_x = oracle.f64_to_bf16_bits(x.double().numpy() + y.double().numpy())
-    got_x = nb(xo)
-    diff = got_x != ref_x
-    assert diff.mean() <= 1e-4
-    assert np.all(np.abs(got_x.astype(np.int32) - ref_x.astype(np.int32))[diff] <= 1)
+    rtol = 2.0 ** -7 if dtype == "bf16" else 2e-6
+    if dtype == "bf16":
+        ref_x = oracle.f64_to_bf16_bits(x.double().numpy() + y.double().numpy())
+        got_x = nb(xo)
+        diff = got_x != ref_x
+        assert diff.mean() <= 1e-4
+        assert np.all(np.abs(got_x.astype(np.int32) - ref_x.astype(np.int32))[diff] <= 1)
+        got_r = oracle.bf16_bits_to_f32(nb(ro)).astype(np.float64)
+    else:
+        got_x = xo.cpu().numpy()
+        np.testing.assert_array_equal(got_x, x.numpy() + y.numpy())
+        got_r = ro.cpu().numpy().astype(np.float64)
     ref_r = oracle.rmsnorm(got_x, 1e-6)
-    got_r = oracle.bf16_bits_to_f32(nb(ro)).astype(np.float64)
-    assert np.all(np.abs(got_r - ref_r) <= 2.0 ** -7 * np.abs(ref_r) + 1e-30)
+    assert np.all(np.abs(got_r - ref_r) <= rtol * np.abs(ref_r) + 1e-30)
     # in place, and without the residual
     x2 = x.to(DEV)
     Lb.moe_residual_rmsnorm(d, x2, None, x2, ro, 1e-6)
     torch.cuda.synchronize()
     assert torch.equal(x2.cpu(), x)
-    got_r = oracle.bf16_bits_to_f32(nb(ro)).astype(np.float64)
-    ref_r = oracle.rmsnorm(nb(x), 1e-6)
-    assert np.all(np.abs(got_r - ref_r) <= 2.0 ** -7 * np.abs(ref_r) + 1e-30)
+    got_r = (oracle.bf16_bits_to_f32(nb(ro)) if dtype == "bf16" else ro.cpu().numpy()).astype(np.float64)
+    ref_r = oracle.rmsnorm(nb(x) if dtype == "bf16" else x.numpy(), 1e-6)
+    assert np.all(np.abs(got_r - ref_r) <= rtol * np.abs(ref_r) + 1e-30)
 
 
 # --------------------------------------------------------------------------- 19-layer stack
