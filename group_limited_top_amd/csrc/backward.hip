@@ -400,22 +400,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_wgrad(const BwdArgs a) {
   const int br = tid >> 3, bc = tid & 7;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   // Rows past the expert's end are loaded from its last row (always a valid
-  // address, no branch) and zeroed when staged.  The token of this lane's B
-  // row k0 + br: wave w's rows are k0 + 8 w .. + 7, read with scalar loads
-  // (they never wait on the data loads' counter) and picked per lane.
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t* const sp_p = uniform_ptr(a.sorted_pair + (sh ? 0 : orow));
-  auto tok_of = [&](int k0) -> int {
-    if (sh) return min(k0 + br, kdim - 1);
-    int v = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int32_t sv = sload(sp_p + min(k0 + 8 * wu + j, kdim - 1));
-      v = (lane >> 3) == j ? sv : v;
-    }
-    return v / K;
-  };
-  auto load = [&](int k0, int tok, u32x4 (&va)[NSEG][NAC], u32x4 (&vb)[4]) __attribute__((always_inline)) {
+  // address, no branch) and zeroed when staged.  The sorted pair of this
+  // lane's B row k0 + br comes from a vector load issued first in the step
+  // two steps before its rows' loads, so waiting for it leaves the newer data
+  // loads in flight (a scalar load here was waited for, a whole L2 round trip,
+  // at every step's barrier).  The shared expert's rows are the tokens
+  // themselves; its pair load is a dummy.
+  auto pair_of = [&](int k0) -> int { return a.sorted_pair[sh ? 0 : orow + min(k0 + br, kdim - 1)]; };
+  auto load = [&](int k0, int pair, u32x4 (&va)[NSEG][NAC], u32x4 (&vb)[4]) __attribute__((always_inline)) {
+    const int tok = sh ? min(k0 + br, kdim - 1) : pair / K;
 #pragma unroll
     for (int sg = 0; sg < NSEG; ++sg)
 #pragma unroll
@@ -490,28 +483,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_wgrad(const BwdArgs a) {
       }
   };
   // Loads two steps ahead of the MFMAs, LDS stores one, nothing in the loop
-  // conditional (as in k_bwd_gemm); the token of a gathered row is read a
-  // step before the row itself.
+  // conditional (as in k_bwd_gemm); step s first loads the pair ids of step
+  // s + 3's rows, then step s + 2's data.
   u32x4 va0[NSEG][NAC], vb0[4], va1[NSEG][NAC], vb1[4];
-  auto step = [&](int st, int& tok_n, u32x4 (&fa)[NSEG][NAC], u32x4 (&fb)[4],
+  auto step = [&](int st, int p_use, int& p_next, u32x4 (&fa)[NSEG][NAC], u32x4 (&fb)[4],
                   const u32x4 (&la)[NSEG][NAC], const u32x4 (&lb)[4]) __attribute__((always_inline)) {
-    load(32 * (st + 2), tok_n, fa, fb);
+    p_next = pair_of(32 * (st + 3));
+    load(32 * (st + 2), p_use, fa, fb);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     // the compute of a step past the end (an odd count) is skipped; it issues
     // no memory loads, so the loads' waits are the same either way
     if (st < nk) compute(st & 1);
-    tok_n = tok_of(32 * (st + 3));
     stage((st + 1) & 1, 32 * (st + 1), la, lb);
     __syncthreads();
   };
-  load(0, tok_of(0), va0, vb0);
+  load(0, pair_of(0), va0, vb0);
   stage(0, 0, va0, vb0);
-  load(32, tok_of(32), va1, vb1);
-  int tok_n = tok_of(64);
+  load(32, pair_of(32), va1, vb1);
+  int pa = pair_of(64), pb = 0;
   __syncthreads();
   for (int st = 0; st < nk; st += 2) {
-    step(st, tok_n, va0, vb0, va1, vb1);
-    step(st + 1, tok_n, va1, vb1, va0, vb0);
+    step(st, pa, pb, va0, vb0, va1, vb1);
+    step(st + 1, pb, pa, va1, vb1, va0, vb0);
   }
   // lane: feature i0 + 16 t + r16, h h0 + 64 wv + 16 j + 4 q .. + 3
   const int q = lane >> 4, r16 = lane & 15;
