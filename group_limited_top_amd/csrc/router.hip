@@ -389,14 +389,31 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, 
   float z[EPL], s[EPL], sb[EPL];
   bool valid[EPL];
   int bad = 0;
-  // issue every partial-sum load first, then add them in split order
+  // issue every partial-sum load first (straight-line: a split past KS
+  // re-reads split 0, an element past E re-reads element E - 1; both are
+  // masked below), then add them in split order.  When every lane's EPL
+  // elements exist (E a multiple of 64 EPL: a wave-uniform test) they are
+  // read as 16-byte pieces.
   float pv[kMaxKSplit][EPL];
+  if (EPL % 4 == 0 && E % (64 * EPL) == 0) {
 #pragma unroll
-  for (int k = 0; k < kMaxKSplit; ++k) {
+    for (int k = 0; k < kMaxKSplit; ++k) {
+      const float* row = part + ((size_t)(k < KS ? k : 0) * T + t) * E + lane * EPL;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane * EPL + i;
-      pv[k][i] = (k < KS && e < E) ? part[((size_t)k * T + t) * E + e] : 0.0f;
+      for (int i = 0; i < EPL; i += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
+        pv[k][i] = v[0];
+        pv[k][i + 1] = v[1];
+        pv[k][i + 2] = v[2];
+        pv[k][i + 3] = v[3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxKSplit; ++k) {
+      const float* row = part + ((size_t)(k < KS ? k : 0) * T + t) * E;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) pv[k][i] = row[min(lane * EPL + i, E - 1)];
     }
   }
 #pragma unroll
@@ -406,7 +423,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, 
 #pragma unroll
     for (int k = 1; k < kMaxKSplit; ++k)
       if (k < KS) acc = acc + pv[k][i];
-    z[i] = acc;
+    z[i] = valid[i] ? acc : 0.0f;
   }
   if (logits_out) {
 #pragma unroll
