@@ -211,21 +211,37 @@ def measure_peaks():
 
 
 def gpu_clocks():
-    """sclk / memory clock / power read with rocm-smi right after the timed
-    region (a child process; None where the tool or a field is unavailable)."""
-    import subprocess
+    """sclk / mclk levels (the current one is marked) and average power of this
+    GPU, read from its sysfs files right after the timed region (no child
+    process: reading files only); None where a file is not there."""
+    import glob
+    import torch
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
-                           capture_output=True, text=True, timeout=30)
-        card = next(iter(json.loads(r.stdout).values()))
+        pr = torch.cuda.get_device_properties(0)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
     except Exception:
         return None
-    keep = {}
-    for k, v in card.items():
-        kl = k.lower()
-        if "sclk" in kl or "mclk" in kl or "power" in kl:
-            keep[k] = v
-    return keep or None
+    base = f"/sys/bus/pci/devices/{bdf}"
+    out = {"pci": bdf}
+
+    def current(name):
+        try:
+            for line in open(f"{base}/{name}"):
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].replace("*", "").strip()
+        except OSError:
+            return None
+        return None
+
+    out["sclk"] = current("pp_dpm_sclk")
+    out["mclk"] = current("pp_dpm_mclk")
+    for f in glob.glob(f"{base}/hwmon/hwmon*/power1_average") + glob.glob(f"{base}/hwmon/hwmon*/power1_input"):
+        try:
+            out["power_W"] = round(int(open(f).read()) / 1e6, 1)
+            break
+        except (OSError, ValueError):
+            pass
+    return out if (out.get("sclk") or out.get("power_W")) else None
 
 
 def verify_logits_run(L, d, shape, xd, weights, ws, y_timed, counts_timed):
