@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec (2048h, 256e top-8) on 1 MI355X; % MFMA / HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MALL_BYTES = 256 * 2 ** 20     # MI355X Infinity Cache
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -551,6 +552,14 @@ def main():
     d = L.desc_from_shape(shape)
     weights = dict(w, w_router=wr.to(dev), expert_bias=None if bias is None else bias.to(dev))
     xd = x.to(dev)
+    # Weights that fit the 256 MB Infinity Cache would be read from it from the
+    # second step on: such a layer's timed steps rotate over copies whose total
+    # exceeds it (step i uses copy i mod n), so every step reads its weights
+    # from HBM as the first one does.
+    wbytes = sum(t.numel() * t.element_size() for t in weights.values() if t is not None)
+    ncopy = 1 if wbytes >= MALL_BYTES else -(-3 * MALL_BYTES // (2 * wbytes)) + 1
+    wsets = [weights] + [{k: (None if t is None else t.clone()) for k, t in weights.items()}
+                         for _ in range(ncopy - 1)]
     y = torch.empty(shape.T, shape.H, dtype=shape.torch_dtype, device=dev)
     counts = torch.empty(shape.E, dtype=torch.int32, device=dev)
     ws = L.alloc_workspace(d, dev)
@@ -564,8 +573,8 @@ def main():
     hev = HipEvents(2 * K)
     pairs = [(hev.ev[2 * i], hev.ev[2 * i + 1]) for i in range(K)]
 
-    for _ in range(W):
-        L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws)
+    for i in range(W):
+        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
     torch.cuda.synchronize()
     # timed region: K steps, each recording an event pair around the dominant
     # kernel on the library's stream
@@ -574,7 +583,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
-        L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws, timed_stage=stage,
+        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws, timed_stage=stage,
                             events=pairs[i])
     t_stop.record()
     torch.cuda.synchronize()
@@ -588,7 +597,7 @@ def main():
     u1 = torch.cuda.Event(enable_timing=True)
     u0.record()
     for i in range(K):
-        L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws)
+        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
     u1.record()
     torch.cuda.synchronize()
     ms_step_plain = u0.elapsed_time(u1) / K
@@ -599,7 +608,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(K):
-                L.moe_layer_forward(d, xd, weights, y, counts_out=counts, ws=ws)
+                L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
         g.replay()  # first replay uploads the graph
         torch.cuda.synchronize()
         g0 = torch.cuda.Event(enable_timing=True)
@@ -643,7 +652,8 @@ def main():
         "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H,
                    "experts": shape.E, "n_group": shape.n_group, "topk_group": shape.topk_group,
                    "top_k": shape.top_k, "moe_intermediate": shape.I,
-                   "shared_intermediate": shape.I_shared, "expert_bias": shape.bias},
+                   "shared_intermediate": shape.I_shared, "expert_bias": shape.bias,
+                   "weight_copies": ncopy},
         "roofline": roof,
         "peaks_measured": peaks,
         "clocks_after_timed_region": clocks,

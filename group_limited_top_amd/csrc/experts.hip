@@ -401,104 +401,182 @@ hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
 }
 
 // ----------------------------------------------------------------------------
-// fp32 variants (small fp32 layers): LDS-tiled fp32 FMA.
+// fp32 variants (small fp32 layers): weight streams on fp32 FMA.  The
+// weights are read once, in 16-byte pieces with eight in flight per thread;
+// only the tile's real rows are computed (a tile of a small layer holds a
+// few rows of its expert), their activations broadcast from LDS.
 // ----------------------------------------------------------------------------
-// gate/up: block = tile rows (32) x 64 intermediate rows; thread = (row, 8 i).
-__global__ __launch_bounds__(256) void k_gateup_f32(const ExpertArgs a, int slices) {
-  __shared__ float xs[kTileRows][65];
-  __shared__ float gs[64][65];
-  __shared__ float us[64][65];
+constexpr int kF32KC = 256;  // K chunk of x staged in LDS (floats)
+constexpr int kF32IC = 256;  // I chunk of h staged in LDS (floats)
+
+// gate/up: block (128 threads) = one tile x 64 features; thread f < 64
+// streams gate row i0 + f, thread 64 + f the up row; the pair meets in LDS for
+// silu(g) u.  Small blocks: several per CU keep more loads in flight.
+__global__ __launch_bounds__(128) void k_gateup_f32(const ExpertArgs a, int slices) {
+  __shared__ __attribute__((aligned(16))) float xs[kTileRows][kF32KC];  // 32 KiB
   const int slice = blockIdx.x % slices;
   TileInfo ti;
   if (!decode_tile(a, blockIdx.x / slices, ti)) return;
   const int I = ti.shared ? a.Is : a.I;
   const int i0 = slice * 64;
-  if (i0 >= I) return;
-  const int H = a.H;
+  if (i0 >= I) return;  // block-uniform
+  const int H = a.H, tid = threadIdx.x;
+  const int f = tid & 63;
+  const bool up = tid >= 64;
+  const bool has_row = i0 + f < I;
   const float* x = reinterpret_cast<const float*>(a.x);
   const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
-  const float* Wg = reinterpret_cast<const float*>(ti.shared ? a.ws_gate : a.w_gate) + ebase;
-  const float* Wu = reinterpret_cast<const float*>(ti.shared ? a.ws_up : a.w_up) + ebase;
-  const int row = threadIdx.x >> 3, cg = threadIdx.x & 7;
-  float accg[8], accu[8];
+  const float* W = reinterpret_cast<const float*>(up ? (ti.shared ? a.ws_up : a.w_up)
+                                                     : (ti.shared ? a.ws_gate : a.w_gate)) +
+                   ebase + (size_t)min(i0 + f, I - 1) * H;
+  const int nrows = ti.nrows;
+  __shared__ int toks[kTileRows];  // the token of each row of the tile
+  if (tid < nrows) toks[tid] = ti.shared ? ti.row0 + tid : a.sorted_pair[ti.row0 + tid] / a.K;
+  __syncthreads();
+  // consecutive FMAs go to different rows: independent chains (with about
+  // one wave per SIMD nothing else hides a dependent FMA's latency)
+  float acc[kTileRows];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) accg[c] = accu[c] = 0.0f;
-  for (int k0 = 0; k0 < H; k0 += 64) {
-    for (int v = threadIdx.x; v < kTileRows * 64; v += 256) {
-      const int r = v >> 6, k = v & 63;
-      float val = 0.0f;
-      if (r < ti.nrows) {
-        const int tok = ti.shared ? ti.row0 + r : a.sorted_pair[ti.row0 + r] / a.K;
-        val = x[(size_t)tok * H + k0 + k];
+  for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+  for (int k0 = 0; k0 < H; k0 += kF32KC) {
+    const int kc = min(kF32KC, H - k0);  // a multiple of 64
+    // x rows of the tile, 16 bytes a piece: every load issued before any
+    // LDS store (a piece past the end re-reads the last one, stored nowhere)
+    {
+      const int n = nrows * (kc / 4);
+      constexpr int kPer = kTileRows * (kF32KC / 4) / 128;
+      f32x4 tmp[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int v = min(tid + 128 * j, n - 1);
+        const int r = v / (kc / 4), c = v % (kc / 4);
+        tmp[j] = *reinterpret_cast<const f32x4*>(x + (size_t)toks[r] * H + k0 + 4 * c);
       }
-      xs[r][k] = val;
-    }
-    for (int v = threadIdx.x; v < 64 * 64; v += 256) {
-      const int i = v >> 6, k = v & 63;
-      gs[i][k] = Wg[(size_t)(i0 + i) * H + k0 + k];
-      us[i][k] = Wu[(size_t)(i0 + i) * H + k0 + k];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int v = tid + 128 * j;
+        if (v < n) *reinterpret_cast<f32x4*>(&xs[v / (kc / 4)][4 * (v % (kc / 4))]) = tmp[j];
+      }
     }
     __syncthreads();
-    for (int k = 0; k < 64; ++k) {
-      const float xv = xs[row][k];
+    if (has_row) {
+      // 32 floats a batch; the next batch's loads are in flight while this
+      // one is used (kc is a multiple of 64: batches come in pairs)
+      f32x4 wa[8], wb[8];
+      auto fetch = [&](f32x4 (&w)[8], int k) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        accg[c] = __builtin_fmaf(xv, gs[cg * 8 + c][k], accg[c]);
-        accu[c] = __builtin_fmaf(xv, us[cg * 8 + c][k], accu[c]);
+        for (int u = 0; u < 8; ++u) w[u] = *reinterpret_cast<const f32x4*>(W + k0 + k + 4 * u);
+      };
+      // rows in groups of 8, one (uniform) test a group: rows past the
+      // tile's end compute on LDS contents nobody stores
+      auto use = [&](const f32x4 (&w)[8], int k) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < kTileRows; g += 8) {
+          if (g >= nrows) continue;  // (not break: the loop must unroll, acc stays in registers)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            f32x4 xv[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) xv[r] = *reinterpret_cast<const f32x4*>(&xs[g + r][k + 4 * u]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int r = 0; r < 8; ++r) acc[g + r] = __builtin_fmaf(w[u][c], xv[r][c], acc[g + r]);
+          }
+        }
+      };
+      fetch(wa, 0);
+      for (int k = 0; k < kc; k += 64) {
+        fetch(wb, k + 32);
+        use(wa, k);
+        if (k + 64 < kc) fetch(wa, k + 64);
+        use(wb, k + 32);
       }
     }
     __syncthreads();
   }
-  if (row < ti.nrows) {
+  // up values to LDS (xs is free after the last barrier), then h = silu(g) u
+  float (*us)[64] = reinterpret_cast<float (*)[64]>(&xs[0][0]);  // [kTileRows][64]
+  if (up) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+      if (r < nrows) us[r][f] = acc[r];
+  }
+  __syncthreads();
+  if (!up && has_row) {
     float* h = reinterpret_cast<float*>(ti.shared ? a.h_shared : a.h_routed);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      h[(size_t)(ti.row0 + row) * I + i0 + cg * 8 + c] = silu_f32(accg[c]) * accu[c];
+    for (int r = 0; r < kTileRows; ++r)
+      if (r < nrows) h[(size_t)(ti.row0 + r) * I + i0 + f] = silu_f32(acc[r]) * us[r][f];
   }
 }
 
-// down: block = tile rows (32) x 256 output columns; thread = (row, 32 columns
-// cg + 8c).
-__global__ __launch_bounds__(256) void k_down_f32(const ExpertArgs a, int hslices) {
-  __shared__ float hsm[kTileRows][33];
-  __shared__ float ws[32][256];
+// down: block (128 threads) = one tile x 512 output columns; thread = 4
+// consecutive columns, streaming down W_down's rows (coalesced 16-byte loads).
+__global__ __launch_bounds__(128) void k_down_f32(const ExpertArgs a, int hslices) {
+  __shared__ __attribute__((aligned(16))) float hsm[kTileRows][kF32IC];  // 32 KiB
   const int hslice = blockIdx.x % hslices;
   TileInfo ti;
   if (!decode_tile(a, blockIdx.x / hslices, ti)) return;
   const int I = ti.shared ? a.Is : a.I;
-  const int H = a.H;
-  const int h0 = hslice * 256;
+  const int H = a.H, tid = threadIdx.x;
+  const int c0 = hslice * 512 + 4 * tid;
+  const bool has_col = c0 < H;  // H is a multiple of 64
   const float* hsrc = reinterpret_cast<const float*>(ti.shared ? a.h_shared : a.h_routed);
   const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
-  const float* Wd = reinterpret_cast<const float*>(ti.shared ? a.ws_down : a.w_down) + ebase;
-  const int row = threadIdx.x >> 3, cg = threadIdx.x & 7;
-  float acc[32];
+  const float* Wd = reinterpret_cast<const float*>(ti.shared ? a.ws_down : a.w_down) + ebase +
+                    min(c0, H - 4);
+  const int nrows = ti.nrows;
+  f32x4 acc[kTileRows];
 #pragma unroll
-  for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-  for (int k0 = 0; k0 < I; k0 += 32) {
-    for (int v = threadIdx.x; v < kTileRows * 32; v += 256) {
-      const int r = v >> 5, k = v & 31;
-      hsm[r][k] = (r < ti.nrows) ? hsrc[(size_t)(ti.row0 + r) * I + k0 + k] : 0.0f;
-    }
-    for (int v = threadIdx.x; v < 32 * 256; v += 256) {
-      const int k = v >> 8, c = v & 255;
-      ws[k][c] = (h0 + c < H) ? Wd[(size_t)(k0 + k) * H + h0 + c] : 0.0f;
+  for (int r = 0; r < kTileRows; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < I; k0 += kF32IC) {
+    const int kc = min(kF32IC, I - k0);  // a multiple of 64
+    {  // every load issued before any LDS store (as in k_gateup_f32)
+      const int n = nrows * (kc / 4);
+      constexpr int kPer = kTileRows * (kF32IC / 4) / 128;
+      f32x4 tmp[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int v = min(tid + 128 * j, n - 1);
+        tmp[j] = *reinterpret_cast<const f32x4*>(hsrc + (size_t)(ti.row0 + v / (kc / 4)) * I + k0 +
+                                                 4 * (v % (kc / 4)));
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int v = tid + 128 * j;
+        if (v < n) *reinterpret_cast<f32x4*>(&hsm[v / (kc / 4)][4 * (v % (kc / 4))]) = tmp[j];
+      }
     }
     __syncthreads();
-    for (int k = 0; k < 32; ++k) {
-      const float hv = hsm[row][k];
+    if (has_col) {
+      for (int k = 0; k < kc; k += 8) {
+        f32x4 w[8];
 #pragma unroll
-      for (int c = 0; c < 32; ++c) acc[c] = __builtin_fmaf(hv, ws[k][cg + 8 * c], acc[c]);
+        for (int u = 0; u < 8; ++u) w[u] = *reinterpret_cast<const f32x4*>(Wd + (size_t)(k0 + k + u) * H);
+        // consecutive FMAs on different rows (independent chains), rows in
+        // groups of 8 with one uniform test a group (as in k_gateup_f32)
+#pragma unroll
+        for (int g = 0; g < kTileRows; g += 8) {
+          if (g >= nrows) continue;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int r = g; r < g + 8; ++r) {
+              const float hv = hsm[r][k + u];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(hv, w[u][c], acc[r][c]);
+            }
+        }
+      }
     }
     __syncthreads();
   }
-  if (row < ti.nrows) {
+  if (has_col) {
     float* o = reinterpret_cast<float*>(ti.shared ? a.o_shared : a.o_routed);
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const int h = h0 + cg + 8 * c;
-      if (h < H) o[(size_t)(ti.row0 + row) * H + h] = acc[c];
-    }
+    for (int r = 0; r < kTileRows; ++r)
+      if (r < nrows) *reinterpret_cast<f32x4*>(o + (size_t)(ti.row0 + r) * H + c0) = acc[r];
   }
 }
 
@@ -529,11 +607,11 @@ hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTim
   const int imax = a.I > a.Is ? a.I : a.Is;
   const int slices = imax / 64;
   stage_begin(tm, kGateUp, s);
-  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
+  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(128), 0, s, a, slices);
   stage_end(tm, kGateUp, s);
-  const int hslices = (a.H + 255) / 256;
+  const int hslices = (a.H + 511) / 512;
   stage_begin(tm, kDown, s);
-  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(256), 0, s, a, hslices);
+  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(128), 0, s, a, hslices);
   stage_end(tm, kDown, s);
   stage_begin(tm, kCombine, s);
   hipLaunchKernelGGL(k_combine_f32, dim3((unsigned)a.T), dim3(256), 0, s, a);

@@ -299,6 +299,30 @@ def test_experts_small(T, dtype, Is):
     assert row_rel(got, ref).max() <= tol
 
 
+@pytest.mark.parametrize("T,H,I,Is,hot", [(300, 320, 192, 192, 0), (200, 512, 320, 64, 0),
+                                           (150, 256, 64, 128, 70), (40, 1088, 128, 0, 40)])
+def test_experts_f32_shapes(T, H, I, Is, hot):
+    """fp32 expert kernels: odd counts of 64-feature slices (I = 192, 320),
+    K chunks of 256 with a partial last one (H = 320, 1088),
+    I chunks of 256 with a partial last one (I = 320), a shared expert of
+    another width, and `hot` tokens all choosing expert 3 (several 32-row
+    tiles of one expert, the last partial)."""
+    say("experts f32", T, H, I, Is, hot)
+    shape = synth.small_shape(T, H=H, I=I, I_shared=Is, dtype="f32", seed=700 + T)
+    dev = make_layer(shape)
+    rng = np.random.default_rng(T + H)
+    idx, w = _random_routing(rng, T, shape.E, shape.top_k)
+    for t in range(hot):
+        if 3 not in idx[t]:
+            idx[t, 0] = 3
+    d = L().desc_from_shape(shape)
+    y = _gpu_experts(d, dev, idx, w)
+    ref = oracle.experts(nb(dev["x"]), idx, w, *oracle_weights(dev))
+    got = to_f64(y)
+    assert rel_l2(got, ref) <= 5e-6
+    assert row_rel(got, ref).max() <= 1e-5
+
+
 def test_experts_full_size_sampled_rows():
     """Full-size shapes (H 2048, I 512), uneven buckets including one expert
     with many rows: every row of a sample of tokens against the oracle."""
