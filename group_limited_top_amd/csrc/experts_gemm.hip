@@ -25,8 +25,8 @@
 // global -> LDS loads (global_load_lds_dwordx4: 1 KiB per wave instruction);
 // five slice buffers (160 KiB, all of the CU's LDS) form a ring, so while a
 // step is computed the next one and a half steps are in flight.  Operands go
-// from LDS to registers one 32-deep half step ahead of the MFMAs that use
-// them (two register sets).
+// from LDS to registers in two 32-deep halves a step: the first half's after
+// the step's barrier, the second half's between the first half's MFMAs.
 //
 // Blocks are persistent (one per CU) and walk a static list of tiles, the
 // ring running on from one tile into the next.  Tiles are ordered expert by
@@ -271,35 +271,48 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
       dn_v = (r16 & 3) ^ wd_swz(r);
     }
   }
-  auto half_step = [&](int g, int h) __attribute__((always_inline)) {
-    const uint8_t* bx = ring + ((2 * g) % kRingN) * kSliceB + lane_b[h];
-    const uint8_t* bw = ring + ((2 * g + 1) % kRingN) * kSliceB + lane_a[h];
-    u32x4 A[8], B[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) B[n] = lds16(bx + 2048 * n);
+  // A step: the operands of its first 32-deep half (B0, A), then that half's
+  // MFMAs with the LDS reads of the second half between them (B1 first; A[i]
+  // is refilled as soon as its four MFMAs are issued), then the second half's
+  // MFMAs.  The second half's reads are thus hidden behind MFMAs; 64 operand
+  // registers where two full sets would need 96.
+  auto read_a = [&](const uint8_t* bw, int i) __attribute__((always_inline)) {
     if (MODE == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        A[i] = lds16(bw + 2048 * i);
-        A[4 + i] = lds16(bw + 16384 + 2048 * i);
-      }
+      return lds16(bw + (i < 4 ? 2048 * i : 16384 + 2048 * (i - 4)));
     } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint8_t* p = bw + 8 * (t & 1) + ((dn_v ^ (4 * (t >> 1))) << 4);
-        const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 512);
-        A[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
+      const uint8_t* p = bw + 8 * (i & 1) + ((dn_v ^ (4 * (i >> 1))) << 4);
+      const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 512);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
     }
-    // raised wave priority while issuing the MFMAs, so that the other wave of
-    // the SIMD issues its LDS reads and loads in between rather than racing
-    // this one for the MFMA pipe
-    __builtin_amdgcn_s_setprio(1);
+  };
+  auto full_step = [&](int g) __attribute__((always_inline)) {
+    const uint8_t* bx = ring + ((2 * g) % kRingN) * kSliceB;
+    const uint8_t* bw = ring + ((2 * g + 1) % kRingN) * kSliceB;
+    u32x4 A[8], B0[4], B1[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) B0[n] = lds16(bx + lane_b[0] + 2048 * n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = read_a(bw + lane_a[0], i);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) B1[n] = lds16(bx + lane_b[1] + 2048 * n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[i][n] = mfma16x16x32(A[i], B0[n], acc[i][n]);
+      A[i] = read_a(bw + lane_a[1], i);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[i][n] = mfma16x16x32(A[i], B[n], acc[i][n]);
-    __builtin_amdgcn_s_setprio(0);
+      for (int n = 0; n < 4; ++n) acc[i][n] = mfma16x16x32(A[i], B1[n], acc[i][n]);
+    // keep that order (the scheduler would otherwise gather the reads)
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, MODE == 0 ? 1 : 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
   };
   // Every epilogue issues the same number of stores per wave (kStores), rows
   // past the tile's end going to trash (the padding rows of h_routed, whose
@@ -387,10 +400,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
       if (g >= 1 && g + 2 < total) issue_x(slot(2 * g + 4));
       stored = ck == 0 && cm > 0;
       if (stored) epilogue(cm - 1);
-      if (wact) {
-        half_step(g, 0);
-        half_step(g, 1);
-      }
+      if (wact) full_step(g);
     }
   }
   epilogue(count - 1);
