@@ -282,35 +282,79 @@ hipError_t launch_logits_bf16(const uint16_t* x, const float* w32, const uint16_
 }
 
 // ----------------------------------------------------------------------------
-// Logits, fp32 activations (small fp32 layers): one block per token, x row in
-// LDS, one thread per expert, fp32 fma in ascending h.
+// Logits, fp32 activations (small fp32 layers).  [Routing §二 step 1]:
+// logit = x . W_r row, fp32.  Block: 4 waves x 8 experts (32 experts), 8
+// tokens.  Lane l of wave v takes expert e0 + 8 v + l / 8 and, of each
+// 512-float chunk of the row, the 16-byte pieces 32 j + 4 (l mod 8) (j < 16):
+// one wave load instruction reads 8 whole 128-byte lines.  The chunk of W
+// sits in registers, the tokens' chunk of x in LDS; each lane sums its
+// products per token (fp32 fma), then the expert's 8 lanes add their sums by
+// an xor butterfly (IEEE addition commutes, so every lane holds the same
+// bits) and lane l stores token l mod 8.
 // ----------------------------------------------------------------------------
+constexpr int kLfTok = 8;      // tokens per block
+constexpr int kLfChunk = 512;  // floats of a row per chunk
+
 __global__ __launch_bounds__(256) void k_logits_f32(const float* __restrict__ x,
                                                      const float* __restrict__ w,
-                                                     float* __restrict__ logits, int H, int E) {
-  extern __shared__ float xs[];
-  const int t = blockIdx.x;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) xs[h] = x[(size_t)t * H + h];
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const float* wr = w + (size_t)e * H;
-    float acc = 0.0f;
-    for (int h = 0; h < H; h += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(wr + h);
-      acc = __builtin_fmaf(xs[h], v.x, acc);
-      acc = __builtin_fmaf(xs[h + 1], v.y, acc);
-      acc = __builtin_fmaf(xs[h + 2], v.z, acc);
-      acc = __builtin_fmaf(xs[h + 3], v.w, acc);
+                                                     float* __restrict__ logits, int T, int H, int E) {
+  __shared__ __attribute__((aligned(16))) float xs[kLfTok][kLfChunk];  // 16 KiB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int t0 = blockIdx.y * kLfTok;
+  const int e = blockIdx.x * 32 + (tid >> 3);  // 8 lanes an expert
+  const int part = lane & 7;
+  const float* wr = w + (size_t)min(e, E - 1) * H + 4 * part;
+  float acc[kLfTok];
+#pragma unroll
+  for (int t = 0; t < kLfTok; ++t) acc[t] = 0.0f;
+  for (int k0 = 0; k0 < H; k0 += kLfChunk) {
+    const int np = min(kLfChunk, H - k0) / 32;  // pieces in this chunk (H % 64 == 0: >= 2)
+    // the chunk of W (pieces past the chunk's end re-read its last piece)
+    f32x4 wv[kLfChunk / 32];
+#pragma unroll
+    for (int j = 0; j < kLfChunk / 32; ++j)
+      wv[j] = *reinterpret_cast<const f32x4*>(wr + k0 + 32 * min(j, np - 1));
+    // the tokens' chunk of x (tokens past T re-read the last token)
+    __syncthreads();  // the previous chunk's readers are done
+#pragma unroll
+    for (int u = 0; u < kLfTok * kLfChunk / 4 / 256; ++u) {
+      const int v = tid + 256 * u;
+      const int t = v / (kLfChunk / 4), c = v % (kLfChunk / 4);
+      if (4 * c < 32 * np)
+        *reinterpret_cast<f32x4*>(&xs[t][4 * c]) =
+            *reinterpret_cast<const f32x4*>(x + (size_t)min(t0 + t, T - 1) * H + k0 + 4 * c);
     }
-    logits[(size_t)t * E + e] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLfChunk / 32; ++j) {
+      if (j >= np) continue;  // uniform
+      f32x4 xv[kLfTok];
+#pragma unroll
+      for (int t = 0; t < kLfTok; ++t) xv[t] = *reinterpret_cast<const f32x4*>(&xs[t][32 * j + 4 * part]);
+      // consecutive FMAs on different tokens: independent chains
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < kLfTok; ++t) acc[t] = __builtin_fmaf(wv[j][c], xv[t][c], acc[t]);
+    }
   }
+  float mine = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kLfTok; ++t) {
+    float v = acc[t];
+    v = v + __shfl_xor(v, 1, 8);
+    v = v + __shfl_xor(v, 2, 8);
+    v = v + __shfl_xor(v, 4, 8);
+    mine = part == t ? v : mine;
+  }
+  if (e < E && t0 + part < T) logits[(size_t)(t0 + part) * E + e] = mine;
 }
 
 hipError_t launch_logits_f32(const float* x, const float* w, float* logits, int T, int H, int E,
                              hipStream_t s, const StageTimer* tm) {
   stage_begin(tm, kLogits, s);
-  hipLaunchKernelGGL(k_logits_f32, dim3((unsigned)T), dim3(256), (size_t)H * sizeof(float), s, x, w,
-                     logits, H, E);
+  const dim3 grid((unsigned)((E + 31) / 32), (unsigned)((T + kLfTok - 1) / kLfTok));
+  hipLaunchKernelGGL(k_logits_f32, grid, dim3(256), 0, s, x, w, logits, T, H, E);
   stage_end(tm, kLogits, s);
   return hipGetLastError();
 }

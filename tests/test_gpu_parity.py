@@ -224,6 +224,30 @@ def test_route_random_ragged_large(T):
     assert stats["decided"] >= 0.9 * T
 
 
+@pytest.mark.parametrize("T,H,E,G,KG,K", [(37, 320, 96, 3, 2, 6), (256, 512, 256, 8, 4, 8),
+                                            (9, 1088, 160, 5, 2, 8), (300, 64, 64, 4, 2, 4)])
+def test_route_random_f32_shapes(T, H, E, G, KG, K):
+    """fp32 activations: logits from random inputs within the band of the
+    oracle's fp64 logits for token counts that end in a partial 8-token block,
+    expert counts that end in a partial 32-expert block (E = 96, 160) and
+    hidden sizes that end in a partial 512-float chunk (H = 320, 1088); the
+    routing then as for the other random inputs."""
+    say("route random f32", T, H, E, G, KG, K)
+    shape = synth.small_shape(T, H=H, I=64, I_shared=0, E=E, n_group=G, topk_group=KG, top_k=K,
+                              dtype="f32", bias="normal", seed=1300 + T)
+    x, wr, b = synth.router_inputs(shape)
+    d = L().desc_from_shape(shape, flags=L().MOE_F_WRITE_LOGITS)
+    idx = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    ws = L().alloc_workspace(d, DEV)
+    L().moe_route(d, x.to(DEV), wr.to(DEV), b.to(DEV), lg, idx, w, ws)
+    torch.cuda.synchronize()
+    l64 = oracle.logits(nb(x), wr.numpy())
+    stats = check_routing_random(d, {"expert_bias": b}, {"logits": lg, "idx": idx, "w": w}, l64)
+    assert stats["decided"] >= 0.9 * T
+
+
 # --------------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,kind", [(1, "uniform"), (77, "uniform"), (512, "uniform"),
