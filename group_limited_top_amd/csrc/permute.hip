@@ -112,6 +112,11 @@ __global__ __launch_bounds__(1024) void k_permute_small(
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int per = ((P + kSmallWaves * 64 - 1) / (kSmallWaves * 64)) * 64;  // pairs per wave
   const int p0 = w * per;
+  // every index load first, straight-line (clamped: a pair past the end
+  // re-reads the last one, unused), so that they are in flight together
+  int32_t raw[kSmallBatches];
+#pragma unroll
+  for (int b = 0; b < kSmallBatches; ++b) raw[b] = idx[min(p0 + b * 64 + lane, P - 1)];
   int32_t rank[kSmallBatches], ev[kSmallBatches];
   int bad = 0;
 #pragma unroll
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(1024) void k_permute_small(
     if (b * 64 < per) {  // block-uniform
       const int p = p0 + b * 64 + lane;
       const bool active = p < P && b * 64 + lane < per;
-      const int32_t e = active ? idx[p] : 0;
+      const int32_t e = active ? raw[b] : 0;
       const bool valid = active && (uint32_t)e < (uint32_t)E;
       bad |= active && !valid;
       const uint64_t same = match_lanes(e, valid, nbits);
@@ -187,17 +192,27 @@ __global__ __launch_bounds__(256) void k_perm_rank(const int32_t* __restrict__ i
   const int sub = ch / 4;
   const int64_t q0 = (int64_t)blockIdx.x * ch + (int64_t)w * sub;
   int bad = 0;
-  for (int b = 0; b < sub; b += 64) {
-    const int64_t p = q0 + b + lane;
-    const bool active = p < P;
-    const int32_t e = active ? idx[p] : 0;
-    const bool valid = active && (uint32_t)e < (uint32_t)E;
-    bad |= active && !valid;
-    const uint64_t same = match_lanes(e, valid, nbits);
-    if (valid) {
-      const int32_t old = cnt[w][e];
-      prank[p] = old + __popcll(same & below);
-      if ((same >> lane) == 1ull) cnt[w][e] = old + __popcll(same);
+  // 8 batches of 64 pairs at a time, their index loads issued together
+  // (clamped: a pair past the end re-reads the last one, unused; sub is a
+  // multiple of 256)
+  for (int b0 = 0; b0 < sub; b0 += 512) {
+    int32_t raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = idx[min(q0 + b0 + 64 * u + lane, P - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b0 + 64 * u >= sub) continue;  // uniform
+      const int64_t p = q0 + b0 + 64 * u + lane;
+      const bool active = p < P;
+      const int32_t e = active ? raw[u] : 0;
+      const bool valid = active && (uint32_t)e < (uint32_t)E;
+      bad |= active && !valid;
+      const uint64_t same = match_lanes(e, valid, nbits);
+      if (valid) {
+        const int32_t old = cnt[w][e];
+        prank[p] = old + __popcll(same & below);
+        if ((same >> lane) == 1ull) cnt[w][e] = old + __popcll(same);
+      }
     }
   }
   __syncthreads();
