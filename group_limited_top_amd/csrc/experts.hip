@@ -409,11 +409,14 @@ hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
 constexpr int kF32KC = 256;  // K chunk of x staged in LDS (floats)
 constexpr int kF32IC = 256;  // I chunk of h staged in LDS (floats)
 
-// gate/up: block (128 threads) = one tile x 64 features; thread f < 64
-// streams gate row i0 + f, thread 64 + f the up row; the pair meets in LDS for
-// silu(g) u.  Small blocks: several per CU keep more loads in flight.
-__global__ __launch_bounds__(128) void k_gateup_f32(const ExpertArgs a, int slices) {
-  __shared__ __attribute__((aligned(16))) float xs[kTileRows][kF32KC];  // 32 KiB
+// gate/up: block (256 threads) = one tile x 64 features; wave v streams the
+// gate (v even) or up (v odd) rows i0 + lane over the first (v < 2) or second
+// half of the K chunks, so that each wave's chain of dependent loads is half
+// as long; the four partial sums meet in LDS (half 0 + half 1, in that order)
+// for silu(g) u.
+__global__ __launch_bounds__(256) void k_gateup_f32(const ExpertArgs a, int slices) {
+  __shared__ __attribute__((aligned(16))) float xs[2][kTileRows][kF32KC];  // 64 KiB
+  __shared__ int toks[kTileRows];  // the token of each row of the tile
   const int slice = blockIdx.x % slices;
   TileInfo ti;
   if (!decode_tile(a, blockIdx.x / slices, ti)) return;
@@ -421,8 +424,8 @@ __global__ __launch_bounds__(128) void k_gateup_f32(const ExpertArgs a, int slic
   const int i0 = slice * 64;
   if (i0 >= I) return;  // block-uniform
   const int H = a.H, tid = threadIdx.x;
-  const int f = tid & 63;
-  const bool up = tid >= 64;
+  const int f = tid & 63, wv = tid >> 6, half = wv >> 1, t128 = tid & 127;
+  const bool up = (wv & 1) != 0;
   const bool has_row = i0 + f < I;
   const float* x = reinterpret_cast<const float*>(a.x);
   const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
@@ -430,36 +433,43 @@ __global__ __launch_bounds__(128) void k_gateup_f32(const ExpertArgs a, int slic
                                                      : (ti.shared ? a.ws_gate : a.w_gate)) +
                    ebase + (size_t)min(i0 + f, I - 1) * H;
   const int nrows = ti.nrows;
-  __shared__ int toks[kTileRows];  // the token of each row of the tile
   if (tid < nrows) toks[tid] = ti.shared ? ti.row0 + tid : a.sorted_pair[ti.row0 + tid] / a.K;
   __syncthreads();
-  // consecutive FMAs go to different rows: independent chains (with about
-  // one wave per SIMD nothing else hides a dependent FMA's latency)
+  // K chunks [0, nh0) to half 0, [nh0, nch) to half 1; both halves take
+  // nh0 rounds of barriers
+  const int nch = (H + kF32KC - 1) / kF32KC, nh0 = (nch + 1) / 2;
+  float (*xh)[kF32KC] = xs[half];
+  // consecutive FMAs go to different rows: independent chains (with few
+  // waves per SIMD nothing else hides a dependent FMA's latency)
   float acc[kTileRows];
 #pragma unroll
   for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
-  for (int k0 = 0; k0 < H; k0 += kF32KC) {
-    const int kc = min(kF32KC, H - k0);  // a multiple of 64
-    // x rows of the tile, 16 bytes a piece: every load issued before any
-    // LDS store (a piece past the end re-reads the last one, stored nowhere)
-    {
+  for (int it = 0; it < nh0; ++it) {
+    const int ch = half == 0 ? it : nh0 + it;
+    const bool mine = ch < nch;  // wave-uniform
+    const int k0 = ch * kF32KC;
+    const int kc = mine ? min(kF32KC, H - k0) : 0;  // a multiple of 64
+    // this half's x rows of the chunk, 16 bytes a piece: every load issued
+    // before any LDS store (a piece past the end re-reads the last one,
+    // stored nowhere)
+    if (mine) {
       const int n = nrows * (kc / 4);
       constexpr int kPer = kTileRows * (kF32KC / 4) / 128;
       f32x4 tmp[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int v = min(tid + 128 * j, n - 1);
+        const int v = min(t128 + 128 * j, n - 1);
         const int r = v / (kc / 4), c = v % (kc / 4);
         tmp[j] = *reinterpret_cast<const f32x4*>(x + (size_t)toks[r] * H + k0 + 4 * c);
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int v = tid + 128 * j;
-        if (v < n) *reinterpret_cast<f32x4*>(&xs[v / (kc / 4)][4 * (v % (kc / 4))]) = tmp[j];
+        const int v = t128 + 128 * j;
+        if (v < n) *reinterpret_cast<f32x4*>(&xh[v / (kc / 4)][4 * (v % (kc / 4))]) = tmp[j];
       }
     }
     __syncthreads();
-    if (has_row) {
+    if (mine && has_row) {
       // 32 floats a batch; the next batch's loads are in flight while this
       // one is used (kc is a multiple of 64: batches come in pairs)
       f32x4 wa[8], wb[8];
@@ -477,7 +487,7 @@ __global__ __launch_bounds__(128) void k_gateup_f32(const ExpertArgs a, int slic
           for (int u = 0; u < 8; ++u) {
             f32x4 xv[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) xv[r] = *reinterpret_cast<const f32x4*>(&xs[g + r][k + 4 * u]);
+            for (int r = 0; r < 8; ++r) xv[r] = *reinterpret_cast<const f32x4*>(&xh[g + r][k + 4 * u]);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -495,19 +505,23 @@ __global__ __launch_bounds__(128) void k_gateup_f32(const ExpertArgs a, int slic
     }
     __syncthreads();
   }
-  // up values to LDS (xs is free after the last barrier), then h = silu(g) u
-  float (*us)[64] = reinterpret_cast<float (*)[64]>(&xs[0][0]);  // [kTileRows][64]
-  if (up) {
+  // partial sums to LDS (xs is free after the last barrier): ps[v][r][f]
+  float (*ps)[kTileRows][64] = reinterpret_cast<float (*)[kTileRows][64]>(&xs[0][0][0]);
+  if (wv != 0) {
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r)
-      if (r < nrows) us[r][f] = acc[r];
+      if (r < nrows) ps[wv][r][f] = acc[r];
   }
   __syncthreads();
-  if (!up && has_row) {
+  if (wv == 0 && has_row) {
     float* h = reinterpret_cast<float*>(ti.shared ? a.h_shared : a.h_routed);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r)
-      if (r < nrows) h[(size_t)(ti.row0 + r) * I + i0 + f] = silu_f32(acc[r]) * us[r][f];
+      if (r < nrows) {
+        const float g = acc[r] + ps[2][r][f];
+        const float u = ps[1][r][f] + ps[3][r][f];
+        h[(size_t)(ti.row0 + r) * I + i0 + f] = silu_f32(g) * u;
+      }
   }
 }
 
@@ -607,7 +621,7 @@ hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTim
   const int imax = a.I > a.Is ? a.I : a.Is;
   const int slices = imax / 64;
   stage_begin(tm, kGateUp, s);
-  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(128), 0, s, a, slices);
+  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
   stage_end(tm, kGateUp, s);
   const int hslices = (a.H + 511) / 512;
   stage_begin(tm, kDown, s);
