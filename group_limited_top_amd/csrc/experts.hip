@@ -525,16 +525,19 @@ __global__ __launch_bounds__(256) void k_gateup_f32(const ExpertArgs a, int slic
   }
 }
 
-// down: block (128 threads) = one tile x 512 output columns; thread = 4
-// consecutive columns, streaming down W_down's rows (coalesced 16-byte loads).
-__global__ __launch_bounds__(128) void k_down_f32(const ExpertArgs a, int hslices) {
+// down: block (4 waves) = one tile x 512 output columns; thread t mod 128 =
+// 4 consecutive columns, streaming W_down's rows (coalesced 16-byte loads);
+// the first two waves take the first half of each I chunk, the other two the
+// second half, so that each wave's chain of dependent loads is half as long.
+// The halves' sums meet in LDS (half 0 + half 1).
+__global__ __launch_bounds__(256) void k_down_f32(const ExpertArgs a, int hslices) {
   __shared__ __attribute__((aligned(16))) float hsm[kTileRows][kF32IC];  // 32 KiB
   const int hslice = blockIdx.x % hslices;
   TileInfo ti;
   if (!decode_tile(a, blockIdx.x / hslices, ti)) return;
   const int I = ti.shared ? a.Is : a.I;
-  const int H = a.H, tid = threadIdx.x;
-  const int c0 = hslice * 512 + 4 * tid;
+  const int H = a.H, tid = threadIdx.x, t128 = tid & 127, half = tid >> 7;
+  const int c0 = hslice * 512 + 4 * t128;
   const bool has_col = c0 < H;  // H is a multiple of 64
   const float* hsrc = reinterpret_cast<const float*>(ti.shared ? a.h_shared : a.h_routed);
   const size_t ebase = ti.shared ? 0 : (size_t)ti.e * a.I * H;
@@ -548,23 +551,24 @@ __global__ __launch_bounds__(128) void k_down_f32(const ExpertArgs a, int hslice
     const int kc = min(kF32IC, I - k0);  // a multiple of 64
     {  // every load issued before any LDS store (as in k_gateup_f32)
       const int n = nrows * (kc / 4);
-      constexpr int kPer = kTileRows * (kF32IC / 4) / 128;
+      constexpr int kPer = kTileRows * (kF32IC / 4) / 256;
       f32x4 tmp[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int v = min(tid + 128 * j, n - 1);
+        const int v = min(tid + 256 * j, n - 1);
         tmp[j] = *reinterpret_cast<const f32x4*>(hsrc + (size_t)(ti.row0 + v / (kc / 4)) * I + k0 +
                                                  4 * (v % (kc / 4)));
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int v = tid + 128 * j;
+        const int v = tid + 256 * j;
         if (v < n) *reinterpret_cast<f32x4*>(&hsm[v / (kc / 4)][4 * (v % (kc / 4))]) = tmp[j];
       }
     }
     __syncthreads();
     if (has_col) {
-      for (int k = 0; k < kc; k += 8) {
+      const int kb = half * (kc / 2), ke = kb + kc / 2;  // this half's k range (multiples of 32)
+      for (int k = kb; k < ke; k += 8) {
         f32x4 w[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) w[u] = *reinterpret_cast<const f32x4*>(Wd + (size_t)(k0 + k + u) * H);
@@ -586,11 +590,30 @@ __global__ __launch_bounds__(128) void k_down_f32(const ExpertArgs a, int hslice
     }
     __syncthreads();
   }
-  if (has_col) {
-    float* o = reinterpret_cast<float*>(ti.shared ? a.o_shared : a.o_routed);
+  // the halves meet, 16 rows a round through hsm (free after the last barrier)
+  f32x4 (*red)[128] = reinterpret_cast<f32x4 (*)[128]>(&hsm[0][0]);  // [16][128]
+  float* o = reinterpret_cast<float*>(ti.shared ? a.o_shared : a.o_routed);
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-      if (r < nrows) *reinterpret_cast<f32x4*>(o + (size_t)(ti.row0 + r) * H + c0) = acc[r];
+  for (int g = 0; g < kTileRows; g += 16) {
+    if (g >= nrows) break;  // block-uniform
+    if (half == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (g + r < nrows) red[r][t128] = acc[g + r];
+    }
+    __syncthreads();
+    if (half == 0 && has_col) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (g + r < nrows) {
+          const f32x4 b = red[r][t128];
+          f32x4 v;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[g + r][c] + b[c];
+          *reinterpret_cast<f32x4*>(o + (size_t)(ti.row0 + g + r) * H + c0) = v;
+        }
+    }
+    __syncthreads();
   }
 }
 
@@ -625,7 +648,7 @@ hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTim
   stage_end(tm, kGateUp, s);
   const int hslices = (a.H + 511) / 512;
   stage_begin(tm, kDown, s);
-  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(128), 0, s, a, hslices);
+  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(256), 0, s, a, hslices);
   stage_end(tm, kDown, s);
   stage_begin(tm, kCombine, s);
   hipLaunchKernelGGL(k_combine_f32, dim3((unsigned)a.T), dim3(256), 0, s, a);
