@@ -618,19 +618,37 @@ __global__ __launch_bounds__(256) void k_down_f32(const ExpertArgs a, int hslice
 }
 
 __global__ __launch_bounds__(256) void k_combine_f32(const ExpertArgs a) {
+  constexpr int kMaxK = 16;  // top_k <= 16 (the supported envelope)
   const int t = blockIdx.x;
   const int H = a.H, K = a.K;
   const float* osh = reinterpret_cast<const float*>(a.o_shared);
   const float* orr = reinterpret_cast<const float*>(a.o_routed);
   float* y = reinterpret_cast<float*>(a.y);
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float acc = (a.Is > 0) ? osh[(size_t)t * H + h] : 0.0f;
-    for (int j = 0; j < K; ++j) {
-      const int32_t slot = a.pair_slot[(size_t)t * K + j];
-      if (slot < 0) continue;
-      acc = acc + a.topk_w[(size_t)t * K + j] * orr[(size_t)slot * H + h];
+  // the token's pair slots and weights, then every row load before any use,
+  // so that the K + 1 loads are in flight together (as in k_combine_bf16)
+  int32_t slot[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;
+    wj[j] = j < K ? a.topk_w[(size_t)t * K + j] : 0.0f;
+  }
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
+    const f32x4 vs = a.Is > 0 ? *reinterpret_cast<const f32x4*>(osh + (size_t)t * H + 4 * c) : zero4;
+    f32x4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      v[j] = slot[j] >= 0 ? *reinterpret_cast<const f32x4*>(orr + (size_t)slot[j] * H + 4 * c) : zero4;
+    // j order, one product and one sum per term, as specified
+    f32x4 acc = vs;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (slot[j] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = acc[i] + wj[j] * v[j][i];
     }
-    y[(size_t)t * H + h] = acc;
+    *reinterpret_cast<f32x4*>(y + (size_t)t * H + 4 * c) = acc;
   }
 }
 
