@@ -10,8 +10,14 @@ call, without the per-launch host and dispatch cost; --eager times steps
 launched one by one instead).  Besides tokens/s it reports the roofline of the
 dominant kernel (its algorithmic bytes or flops per launch over its average
 duration, timed with HIP events recorded on the library's stream around that
-kernel in every step of an eager timed loop of K steps) and the CPU oracle
-timed on this host (`cpu_baseline`).
+kernel in every step of an eager timed loop of K steps), the layer's fraction
+of the HBM and bf16 MFMA peaks against its target, and the CPU oracle timed on
+this host (`cpu_baseline`).
+
+The default workload (512 tokens: the weight-streaming, HBM-bound regime) is
+the headline; the same run measures the 16384-token layer with an expert bias
+(`large_batch`) and the 65536-token layer with skewed routing (`skew`), the
+MFMA regime, each with its own roofline, target and CPU baseline.
 """
 import argparse
 import json
@@ -338,7 +344,10 @@ def synth_weights(shape, layer):
 
 def cpu_baseline(shape, x, wr, bias, w, max_tokens):
     """The oracle as it stands: routing for every token, experts + combine for
-    the first `max_tokens` tokens; throughput scaled to tokens/s."""
+    a bounded sample of tokens; throughput scaled to tokens/s.  The sample is
+    the first `max_tokens` tokens, or for more than 16384 tokens the first
+    `max_tokens` tokens t = 0 (mod 8) (an extrapolation from that sample).
+    Up to 4096 tokens the same sample is also timed on one thread."""
     import numpy as np
     import oracle
     from group_limited_top_amd import synth
@@ -353,22 +362,16 @@ def cpu_baseline(shape, x, wr, bias, w, max_tokens):
     idx, tw, _, _ = oracle.route(xb, wrb, b, shape.n_group, shape.topk_group, shape.top_k,
                                  shape.scale, threads)
     t_route = time.perf_counter() - t0
-    n = min(max_tokens, shape.T)
-    tok = np.arange(n, dtype=np.int32)
+    stride = 8 if shape.T > 16384 else 1
+    tok = np.arange(0, shape.T, stride, dtype=np.int32)[:max_tokens]
+    n = tok.size
     t0 = time.perf_counter()
     oracle.experts(xb, idx, tw, *ow, tokens=tok, nthreads=threads)
     t_exp = time.perf_counter() - t0
     per_token = t_route / shape.T + t_exp / n
+    which = f"the first {n} tokens" if stride == 1 else f"{n} tokens t = 0 (mod 8), extrapolated"
     sample = (f"routing of all {shape.T} tokens ({t_route:.2f} s) + experts and combine of "
-              f"{n} tokens ({t_exp:.2f} s), scaled per token")
-    # the same sample on one thread
-    t0 = time.perf_counter()
-    oracle.route(xb, wrb, b, shape.n_group, shape.topk_group, shape.top_k, shape.scale, 1)
-    t_route1 = time.perf_counter() - t0
-    n1 = min(n, 64)
-    t0 = time.perf_counter()
-    oracle.experts(xb, idx, tw, *ow, tokens=tok[:n1], nthreads=1)
-    t_exp1 = time.perf_counter() - t0
+              f"{which} ({t_exp:.2f} s), scaled per token")
     cpu = None
     try:
         for line in open("/proc/cpuinfo"):
@@ -377,11 +380,20 @@ def cpu_baseline(shape, x, wr, bias, w, max_tokens):
                 break
     except OSError:
         pass
-    return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "sample": sample,
-            "value_1thread": round(1.0 / (t_route1 / shape.T + t_exp1 / n1), 2),
-            "sample_1thread": f"routing of all {shape.T} tokens + experts and combine of {n1} tokens",
-            "cpu_model": cpu, "nproc": os.cpu_count()}
+    out = {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": threads,
+           "kind": "oracle", "sample": sample, "cpu_model": cpu, "nproc": os.cpu_count()}
+    if shape.T <= 4096:
+        # the same sample on one thread
+        t0 = time.perf_counter()
+        oracle.route(xb, wrb, b, shape.n_group, shape.topk_group, shape.top_k, shape.scale, 1)
+        t_route1 = time.perf_counter() - t0
+        n1 = min(n, 64)
+        t0 = time.perf_counter()
+        oracle.experts(xb, idx, tw, *ow, tokens=tok[:n1], nthreads=1)
+        t_exp1 = time.perf_counter() - t0
+        out["value_1thread"] = round(1.0 / (t_route1 / shape.T + t_exp1 / n1), 2)
+        out["sample_1thread"] = f"routing of all {shape.T} tokens + experts and combine of {n1} tokens"
+    return out
 
 
 def bench_balance(L, d, shape, xd, weights, ws, K):
@@ -489,6 +501,166 @@ def bench_backward(L, d, shape, xd, weights, K):
             "grad_write_GBs": round(grad_bytes / (us * 1e-6) / 1e9, 1)}
 
 
+TARGETS = {  # the layer fraction each regime is held to
+    "hbm": ("layer_hbm_frac", 0.60),
+    "mfma": ("layer_mfma_frac", 0.50),
+}
+
+
+def layer_inputs(L, shape, dev):
+    """Seeded synthetic inputs of a single-layer workload, on the GPU."""
+    from group_limited_top_amd import synth
+    x, wr, bias = synth.router_inputs(shape)
+    if shape.bias == "skew":
+        bias = synth.skew_bias()
+    w = synth.expert_weights(shape, device=dev)
+    weights = dict(w, w_router=wr.to(dev), expert_bias=None if bias is None else bias.to(dev))
+    return x, wr, bias, w, weights
+
+
+def bench_layer(L, shape, K, W, eager=False, balance=True, backward=True, cpu=True,
+                cpu_tokens=512, peaks=None):
+    """One single-layer workload: K timed steps (see the module docstring).
+    Returns the JSON object of that workload (the bench line's fields)."""
+    import torch
+    dev = "cuda"
+    x, wr, bias, w, weights = layer_inputs(L, shape, dev)
+    d = L.desc_from_shape(shape)
+    xd = x.to(dev)
+    # Weights that fit the 256 MB Infinity Cache would be read from it from the
+    # second step on: such a layer's timed steps rotate over copies whose total
+    # exceeds it (step i uses copy i mod n), so every step reads its weights
+    # from HBM as the first one does.
+    wbytes = sum(t.numel() * t.element_size() for t in weights.values() if t is not None)
+    ncopy = 1 if wbytes >= MALL_BYTES else -(-3 * MALL_BYTES // (2 * wbytes)) + 1
+    wsets = [weights] + [{k: (None if t is None else t.clone()) for k, t in weights.items()}
+                         for _ in range(ncopy - 1)]
+    y = torch.empty(shape.T, shape.H, dtype=shape.torch_dtype, device=dev)
+    counts = torch.empty(shape.E, dtype=torch.int32, device=dev)
+    ws = L.alloc_workspace(d, dev)
+    stage = "gate_up"
+    hev = HipEvents(2 * K)
+    pairs = [(hev.ev[2 * i], hev.ev[2 * i + 1]) for i in range(K)]
+
+    for i in range(W):
+        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
+    torch.cuda.synchronize()
+    # timed region: K steps, each recording an event pair around the dominant
+    # kernel on the library's stream
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws, timed_stage=stage,
+                            events=pairs[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_stop) / K
+    kern_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / K
+    hev.close()
+    # the same K steps with no event inside a step, for reference
+    u0 = torch.cuda.Event(enable_timing=True)
+    u1 = torch.cuda.Event(enable_timing=True)
+    u0.record()
+    for i in range(K):
+        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
+    u1.record()
+    torch.cuda.synchronize()
+    ms_step_plain = u0.elapsed_time(u1) / K
+    ms_step_graph = None
+    if not eager:
+        # the K steps captured in one HIP graph and replayed: the same kernels,
+        # without the per-launch host and dispatch cost
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_step_graph = g0.elapsed_time(g1) / K
+        del g
+    assert L.moe_status(ws) == 0
+    clocks = gpu_clocks()
+    verification = verify_logits_run(L, d, shape, xd, weights, ws, y, counts)
+
+    work = algorithmic_work(shape, counts.cpu().numpy())
+    ms_value = ms_step_graph if ms_step_graph is not None else ms_step
+    tokens_per_s = shape.T / (ms_value * 1e-3)
+    if shape.T >= 4096:
+        achieved = work["flops_gate_up"] / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = work["k_gate_up"] / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    if peaks:
+        mp = peaks["bf16_mfma_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_read_GBs"]
+        roof["measured_peak"] = mp
+        roof["frac_vs_measured"] = round(roof["achieved"] / mp, 4)
+    kname = L.moe_stage_kernel(d, stage)
+    roof["traffic"] = measured_traffic(shape.name, kname)
+    roof.update(kernel=kname,
+                kernel_ms=round(kern_ms, 4), algorithmic_bytes=work["k_gate_up"],
+                algorithmic_flops=work["flops_gate_up"])
+    layer_hbm = work["layer"] / (ms_value * 1e-3) / 1e9
+    layer_tflops = work["flops_layer"] / (ms_value * 1e-3) / 1e12
+    layer = {"algorithmic_bytes": work["layer"], "algorithmic_flops": work["flops_layer"],
+             "hbm_GBs": round(layer_hbm, 1), "hbm_frac": round(layer_hbm / HBM_PEAK_GBS, 4),
+             "tflops": round(layer_tflops, 2),
+             "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
+             "experts_hit": work["hit"], "max_expert_rows": int(counts.max().item())}
+    tname, tval = TARGETS[roof["bound"]]
+    got = layer["mfma_frac"] if roof["bound"] == "mfma" else layer["hbm_frac"]
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms_value, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype, "data": "synthetic",
+        "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H,
+                   "experts": shape.E, "n_group": shape.n_group, "topk_group": shape.topk_group,
+                   "top_k": shape.top_k, "moe_intermediate": shape.I,
+                   "shared_intermediate": shape.I_shared, "expert_bias": shape.bias,
+                   "weight_copies": ncopy},
+        "roofline": roof,
+        "layer": layer,
+        "target": {tname: tval, "achieved": got, "met": bool(got >= tval),
+                   "ms_per_step_at_target": round(
+                       (work["flops_layer"] / (tval * BF16_PEAK_TFLOPS * 1e12) if roof["bound"] == "mfma"
+                        else work["layer"] / (tval * HBM_PEAK_GBS * 1e9)) * 1e3, 4)},
+        "clocks_after_timed_region": clocks,
+        "verification": verification,
+        "wall_s_timed": round(wall, 4),
+        "timing": {"value_from": "graph" if ms_step_graph is not None else "eager",
+                   "ms_per_step_graph": None if ms_step_graph is None else round(ms_step_graph, 4),
+                   "ms_per_step_eager_with_kernel_events": round(ms_step, 4),
+                   "ms_per_step_eager": round(ms_step_plain, 4)},
+    }
+    if balance:
+        out["balance"] = bench_balance(L, d, shape, xd, weights, ws, K)
+    if backward and shape.dtype == "bf16":
+        out["backward"] = bench_backward(L, d, shape, xd, weights, min(K, 10))
+    del ws, wsets, y
+    torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline(shape, x, wr, bias, w, cpu_tokens)
+    return out
+
+
+# The default run: the 512-token layer (HBM-bound weight stream) is the
+# headline; the 16384-token layer with bias and the 65536-token skewed layer
+# (the MFMA regime) are measured in the same run, each with its own roofline
+# and CPU baseline.
+EXTRA_WORKLOADS = (("large_batch", "full_t16k_bias"), ("skew", "skew_t64k"))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -500,6 +672,8 @@ def main():
                     help="time steps launched one by one instead of a HIP graph of K steps")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="with the default workload: skip the 16384- and 65536-token layers")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the streaming-read and MFMA rates of this GPU")
     ap.add_argument("--backward-only", action="store_true",
@@ -537,142 +711,33 @@ def main():
     from group_limited_top_amd import synth
 
     shape = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
     if shape.layers != 1:
-        torch.cuda.set_device(0)
         print(json.dumps(bench_stack(L, shape, min(args.steps, 10), min(args.warmup, 2))), flush=True)
         return
-    dev = "cuda"
-    torch.cuda.set_device(0)
-    x, wr, bias = synth.router_inputs(shape)
-    if shape.bias == "skew":
-        bias_path = os.path.join(ROOT, "tests", "golden", "skew_t64k_expert_bias.txt")
-        import numpy as np
-        bias = torch.from_numpy(np.loadtxt(bias_path, dtype=np.float32))
-    w = synth.expert_weights(shape, device=dev)
-    d = L.desc_from_shape(shape)
-    weights = dict(w, w_router=wr.to(dev), expert_bias=None if bias is None else bias.to(dev))
-    xd = x.to(dev)
-    # Weights that fit the 256 MB Infinity Cache would be read from it from the
-    # second step on: such a layer's timed steps rotate over copies whose total
-    # exceeds it (step i uses copy i mod n), so every step reads its weights
-    # from HBM as the first one does.
-    wbytes = sum(t.numel() * t.element_size() for t in weights.values() if t is not None)
-    ncopy = 1 if wbytes >= MALL_BYTES else -(-3 * MALL_BYTES // (2 * wbytes)) + 1
-    wsets = [weights] + [{k: (None if t is None else t.clone()) for k, t in weights.items()}
-                         for _ in range(ncopy - 1)]
-    y = torch.empty(shape.T, shape.H, dtype=shape.torch_dtype, device=dev)
-    counts = torch.empty(shape.E, dtype=torch.int32, device=dev)
-    ws = L.alloc_workspace(d, dev)
     if args.backward_only:
+        _, _, _, _, weights = layer_inputs(L, shape, "cuda")
+        x = synth.router_inputs(shape)[0].to("cuda")
+        d = L.desc_from_shape(shape)
         print(json.dumps({"workload": shape.name,
-                          "backward": bench_backward(L, d, shape, xd, weights, min(args.steps, 10))}),
+                          "backward": bench_backward(L, d, shape, x, weights, min(args.steps, 10))}),
               flush=True)
         return
-    stage = "gate_up"
-    K, W = args.steps, args.warmup
-    hev = HipEvents(2 * K)
-    pairs = [(hev.ev[2 * i], hev.ev[2 * i + 1]) for i in range(K)]
-
-    for i in range(W):
-        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
-    torch.cuda.synchronize()
-    # timed region: K steps, each recording an event pair around the dominant
-    # kernel on the library's stream
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(K):
-        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws, timed_stage=stage,
-                            events=pairs[i])
-    t_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_stop)
-    ms_step = ms_total / K
-    kern_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / K
-    hev.close()
-    # the same K steps with no event inside a step, for reference
-    u0 = torch.cuda.Event(enable_timing=True)
-    u1 = torch.cuda.Event(enable_timing=True)
-    u0.record()
-    for i in range(K):
-        L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
-    u1.record()
-    torch.cuda.synchronize()
-    ms_step_plain = u0.elapsed_time(u1) / K
-    ms_step_graph = None
-    if not args.eager:
-        # the K steps captured in one HIP graph and replayed: the same kernels,
-        # without the per-launch host and dispatch cost
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(K):
-                L.moe_layer_forward(d, xd, wsets[i % ncopy], y, counts_out=counts, ws=ws)
-        g.replay()  # first replay uploads the graph
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        ms_step_graph = g0.elapsed_time(g1) / K
-    assert L.moe_status(ws) == 0
-    clocks = gpu_clocks()
-    verification = verify_logits_run(L, d, shape, xd, weights, ws, y, counts)
-
-    work = algorithmic_work(shape, counts.cpu().numpy())
-    ms_value = ms_step_graph if ms_step_graph is not None else ms_step
-    tokens_per_s = shape.T / (ms_value * 1e-3)
-    if shape.T >= 4096:
-        achieved = work["flops_gate_up"] / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        achieved = work["k_gate_up"] / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     peaks = None if args.no_peaks else measure_peaks()
-    if peaks:
-        mp = peaks["bf16_mfma_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_read_GBs"]
-        roof["measured_peak"] = mp
-        roof["frac_vs_measured"] = round(roof["achieved"] / mp, 4)
-    kname = L.moe_stage_kernel(d, stage)
-    roof["traffic"] = measured_traffic(shape.name, kname)
-    roof.update(kernel=kname,
-                kernel_ms=round(kern_ms, 4), algorithmic_bytes=work["k_gate_up"],
-                algorithmic_flops=work["flops_gate_up"])
-    layer_hbm = work["layer"] / (ms_value * 1e-3) / 1e9
-    layer_tflops = work["flops_layer"] / (ms_value * 1e-3) / 1e12
-    out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": K, "warmup": W, "ms_per_step": round(ms_value, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype, "data": "synthetic",
-        "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H,
-                   "experts": shape.E, "n_group": shape.n_group, "topk_group": shape.topk_group,
-                   "top_k": shape.top_k, "moe_intermediate": shape.I,
-                   "shared_intermediate": shape.I_shared, "expert_bias": shape.bias,
-                   "weight_copies": ncopy},
-        "roofline": roof,
-        "peaks_measured": peaks,
-        "clocks_after_timed_region": clocks,
-        "verification": verification,
-        "layer": {"algorithmic_bytes": work["layer"], "hbm_GBs": round(layer_hbm, 1),
-                  "hbm_frac": round(layer_hbm / HBM_PEAK_GBS, 4), "tflops": round(layer_tflops, 2),
-                  "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
-                  "experts_hit": work["hit"]},
-        "wall_s_timed": round(wall, 4),
-        "timing": {"value_from": "graph" if ms_step_graph is not None else "eager",
-                   "ms_per_step_graph": None if ms_step_graph is None else round(ms_step_graph, 4),
-                   "ms_per_step_eager_with_kernel_events": round(ms_step, 4),
-                   "ms_per_step_eager": round(ms_step_plain, 4)},
-    }
-    out["balance"] = bench_balance(L, d, shape, xd, weights, ws, K)
-    if shape.dtype == "bf16" and not args.no_backward:
-        out["backward"] = bench_backward(L, d, shape, xd, weights, min(K, 10))
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, x, wr, bias, w, args.cpu_tokens)
+    out = bench_layer(L, shape, args.steps, args.warmup, eager=args.eager,
+                      backward=not args.no_backward, cpu=not args.no_cpu_baseline,
+                      cpu_tokens=args.cpu_tokens, peaks=peaks)
+    out["peaks_measured"] = peaks
+    if args.workload == "full_t512" and not args.no_extra_workloads:
+        for key, name in EXTRA_WORKLOADS:
+            out[key] = bench_layer(L, synth.WORKLOADS[name], min(args.steps, 20),
+                                   min(args.warmup, 5), eager=args.eager, balance=False,
+                                   backward=False,
+                                   cpu=not args.no_cpu_baseline, cpu_tokens=args.cpu_tokens,
+                                   peaks=peaks)
+            for k in ("metric", "unit", "n_gpus", "higher_is_better", "scaling", "vs_baseline",
+                      "data"):
+                out[key].pop(k)
     print(json.dumps(out), flush=True)
 
 

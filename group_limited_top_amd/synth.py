@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 
 import torch
 
@@ -97,8 +98,8 @@ def skew_offsets(E: int, n_group: int, seed: int, hot_groups: int = 2, hot_per_g
 
 def router_inputs(shape: LayerShape, layer: int = 0):
     """(x [T,H], router weight [E,H] fp32, expert bias [E] fp32 or None) on the
-    CPU.  For the skewed workload the bias is returned as None: it is derived
-    from the first routing pass (see ``skew_bias_from_counts``)."""
+    CPU.  For the skewed workload the bias is returned as None: it comes from
+    the first routing pass and is stored with the tests (``skew_bias``)."""
     B = shape.seed + 100 * layer
     x = _normal((shape.T, shape.H), 1.0, B + 0, "cpu", shape.torch_dtype)
     wr = _normal((shape.E, shape.H), 1.0 / math.sqrt(shape.H), B + 1, "cpu", torch.float32)
@@ -112,14 +113,16 @@ def router_inputs(shape: LayerShape, layer: int = 0):
     return x, wr, bias
 
 
-def skew_bias_from_counts(counts, T: int, top_k: int) -> torch.Tensor:
-    """Bias that partly rebalances a skewed routing: -0.1 times the per-expert
-    hit-count excess over the mean, normalised by the largest excess."""
-    c = torch.as_tensor(counts, dtype=torch.float64)
-    m = T * top_k / c.numel()
-    ex = c - m
-    denom = ex.abs().max().clamp_min(1.0)
-    return (-0.1 * ex / denom).to(torch.float32)
+SKEW_BIAS_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                              "tests", "golden", "skew_t64k_expert_bias.txt")
+
+
+def skew_bias() -> torch.Tensor:
+    """The skewed workload's expert bias [E] fp32, as stored next to the tests
+    (the load-balancing update of the first, unbiased routing pass's counts;
+    tests/golden/make_skew_bias.py writes it from the oracle)."""
+    vals = [float(line) for line in open(SKEW_BIAS_FILE) if line.strip() and line[0] != "#"]
+    return torch.tensor(vals, dtype=torch.float32)
 
 
 def expert_weights(shape: LayerShape, device="cpu", layer: int = 0):

@@ -69,6 +69,7 @@ def _load():
     lib.orc_sigmoid32.restype = ctypes.c_float
     lib.orc_sigmoid32_array.argtypes = [P, P, i64]
     lib.orc_sigmoid32_scan.argtypes = [u64, u64, u64, i32, P]
+    lib.orc_sigmoid32_compare.argtypes = [u64, u64, P, i32, P]
     lib.orc_logits.argtypes = [i32, i32, i32, P, i32, P, P, i32]
     lib.orc_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_float, P, P, P, P, P]
     lib.orc_select.restype = i32
@@ -133,6 +134,17 @@ def sigmoid32(z) -> np.ndarray:
     out = np.empty_like(z)
     _load().orc_sigmoid32_array(_ptr(z), _ptr(out), z.size)
     return out
+
+
+def sigmoid32_compare(start: int, other: np.ndarray, nthreads: int | None = None):
+    """(mismatches, first mismatching index or -1) of sigma32 over the fp32 bit
+    patterns start .. start + len(other) - 1 against ``other`` (another
+    implementation's results for those patterns; NaN matches any NaN)."""
+    other = np.ascontiguousarray(other, dtype=np.float32)
+    out = np.zeros(2, dtype=np.int64)
+    _load().orc_sigmoid32_compare(start, other.size, _ptr(other), nthreads or default_threads(),
+                                  _ptr(out))
+    return int(out[0]), int(out[1])
 
 
 def sigmoid32_scan(start: int, stop: int, stride: int, nthreads: int | None = None):

@@ -196,6 +196,56 @@ void orc_sigmoid32_scan(uint64_t start, uint64_t stop, uint64_t stride, int nthr
   free(th);
 }
 
+/* --- sigma32 of every bit pattern in a range, compared with another's ---- */
+
+typedef struct {
+  uint64_t start, n;        /* bit patterns start .. start + n - 1 */
+  const float* other;       /* other[i] is the other side's sigma32(pattern start + i) */
+  int64_t mismatches, first;
+} cmp_job_t;
+
+static void* cmp_worker(void* arg) {
+  cmp_job_t* j = (cmp_job_t*)arg;
+  j->mismatches = 0;
+  j->first = -1;
+  for (uint64_t i = 0; i < j->n; ++i) {
+    float s = orc_sigmoid32(bits_to_float((uint32_t)(j->start + i)));
+    float o = j->other[i];
+    int same = float_to_bits(s) == float_to_bits(o) || (s != s && o != o);
+    if (!same) {
+      if (j->first < 0) j->first = (int64_t)i;
+      ++j->mismatches;
+    }
+  }
+  return NULL;
+}
+
+void orc_sigmoid32_compare(uint64_t start, uint64_t n, const float* other, int nthreads,
+                           int64_t out[2]) {
+  if (nthreads < 1) nthreads = 1;
+  cmp_job_t* jobs = (cmp_job_t*)calloc((size_t)nthreads, sizeof(cmp_job_t));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  uint64_t per = (n + (uint64_t)nthreads - 1) / (uint64_t)nthreads;
+  for (int i = 0; i < nthreads; ++i) {
+    uint64_t a = (uint64_t)i * per, e = a + per;
+    if (a > n) a = n;
+    if (e > n) e = n;
+    jobs[i].start = start + a;
+    jobs[i].n = e - a;
+    jobs[i].other = other + a;
+    pthread_create(&th[i], NULL, cmp_worker, &jobs[i]);
+  }
+  out[0] = 0;
+  out[1] = -1;
+  for (int i = 0; i < nthreads; ++i) {
+    pthread_join(th[i], NULL);
+    out[0] += jobs[i].mismatches;
+    if (out[1] < 0 && jobs[i].first >= 0) out[1] = (int64_t)((uint64_t)i * per) + jobs[i].first;
+  }
+  free(jobs);
+  free(th);
+}
+
 /* ------------------------------------------------------------------------ */
 /* thread helper: run fn(ctx, t0, t1) over [0, n) split into contiguous chunks */
 /* ------------------------------------------------------------------------ */

@@ -40,6 +40,13 @@ void orc_sigmoid32_array(const float* z, float* s, int64_t n);
 void orc_sigmoid32_scan(uint64_t start, uint64_t stop, uint64_t stride, int nthreads,
                         int64_t out[4]);
 
+/* sigma32 of the n fp32 bit patterns start .. start + n - 1 compared with
+ * other[0 .. n-1] (another implementation's results for the same patterns):
+ * out[0] = patterns whose results differ (bits differ and not both NaN),
+ * out[1] = index of the first such pattern, or -1. */
+void orc_sigmoid32_compare(uint64_t start, uint64_t n, const float* other, int nthreads,
+                           int64_t out[2]);
+
 /* R1: router logits l[t][e] = sum_h x[t][h]*w_router[e][h] in fp64. */
 void orc_logits(int T, int H, int E, const void* x, int xdt, const float* w_router,
                 double* logits, int nthreads);

@@ -1,6 +1,7 @@
 """Writes tests/golden/skew_t64k_expert_bias.txt: the expert bias of the skewed
 65536-token workload, derived from the oracle's first routing pass (no bias)
-over that workload's synthetic router inputs:
+over that workload's synthetic router inputs, by the oracle's expert-bias
+update from a zero bias at rate 0.1:
     bias_e = -0.1 * (count_e - mean) / max_e |count_e - mean|,  mean = T*k/E.
 Calls only oracle/ and the seeded input generator.
 
@@ -24,8 +25,8 @@ def skew_bias():
     idx, _, flag, _ = oracle.route(synth.to_numpy_bits(x), wr.numpy(), None, shape.n_group,
                                    shape.topk_group, shape.top_k, shape.scale)
     assert not flag.any()
-    counts = np.bincount(idx.reshape(-1), minlength=shape.E)
-    bias = synth.skew_bias_from_counts(counts, shape.T, shape.top_k).numpy()
+    counts = np.bincount(idx.reshape(-1), minlength=shape.E).astype(np.int32)
+    bias = oracle.bias_update(counts, None, 0.1)
     return counts, bias
 
 

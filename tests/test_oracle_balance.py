@@ -105,12 +105,16 @@ def test_bias_update_invariants():
 
 
 def test_bias_update_from_zero_is_the_skewed_workload_bias():
+    """The skewed workload's bias recipe, -0.1 (c_e - m) / max_e |c_e - m| with
+    m = T k / E (evaluated here in numpy fp64, one rounding to fp32), is the
+    oracle's update from a zero bias at rate 0.1."""
     rng = np.random.default_rng(3)
     c = rng.integers(0, 5000, 256).astype(np.int32)
     T = int(c.sum()) // 8
     c[0] += T * 8 - int(c.sum())
-    np.testing.assert_array_equal(oracle.bias_update(c, None, 0.1),
-                                  synth.skew_bias_from_counts(c, T, 8).numpy())
+    ex = c.astype(np.float64) - T * 8 / 256
+    recipe = ((-0.1 * ex) / max(np.abs(ex).max(), 1.0)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.bias_update(c, None, 0.1), recipe)
 
 
 def test_balancing_loop_spreads_a_skewed_routing():
