@@ -26,8 +26,10 @@ EXPORTS = (
     "moe_residual_rmsnorm", "moe_status", "moe_sigmoid32", "moe_strerror",
     "moe_layer_forward_timed", "moe_stage_kernel", "moe_expert_stats", "moe_bias_update",
     "moe_aux_loss_workspace_size", "moe_aux_loss", "moe_backward_workspace_size",
-    "moe_layer_backward",
+    "moe_layer_backward", "moe_layer_forward_noalloc",
 )
+MOE_ERR_SCRATCH = -6
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # the static buffer of moe_layer_forward_noalloc
 MOE_NSTAT = 8
 STAT_NAMES = ("hits", "max_load", "min_load", "cv", "idle", "hottest", "coldest",
               "max_group_load")
@@ -77,6 +79,8 @@ def _load():
     lib.moe_experts.restype = i
     lib.moe_layer_forward.argtypes = [D, P, W, P, P, P, P, P, P, P, S, P]
     lib.moe_layer_forward.restype = i
+    lib.moe_layer_forward_noalloc.argtypes = [D, P, W, P, P, P, P, P, P, P]
+    lib.moe_layer_forward_noalloc.restype = i
     lib.moe_layer_forward_timed.argtypes = [D, P, W, P, P, P, P, P, P, P, S, P, i, P, P]
     lib.moe_layer_forward_timed.restype = i
     lib.moe_residual_rmsnorm.argtypes = [D, P, P, P, P, ctypes.c_float, P]
@@ -281,6 +285,28 @@ def moe_layer_forward(d: MoeDesc, x, weights: dict, y, topk_idx_out=None, topk_w
                                     _stream(stream), STAGES.index(timed_stage),
                                     ctypes.c_void_p(ev0), ctypes.c_void_p(ev1)),
         "moe_layer_forward_timed")
+
+
+def moe_layer_forward_noalloc(d: MoeDesc, x, weights: dict, y, topk_idx_out=None,
+                              topk_w_out=None, logits_out=None, counts_out=None, tracking=None,
+                              stream=None):
+    """The whole layer with the library's static per-device scratch buffer
+    instead of a workspace (no device allocation anywhere in the call)."""
+    dev = x.device
+    T, H, E, K = d.T, d.H, d.E, d.top_k
+    dt = _act_dtype(d)
+    xp = _check(x, "x", (T, H), dt, dev)
+    W = _weights(d, weights, dev, need_router=True)
+    args = (
+        _check(y, "y", (T, H), dt, dev),
+        _check(topk_idx_out, "topk_idx_out", (T, K), torch.int32, dev, optional=True),
+        _check(topk_w_out, "topk_w_out", (T, K), torch.float32, dev, optional=True),
+        _check(logits_out, "logits_out", (T, E), torch.float32, dev, optional=True),
+        _check(counts_out, "counts_out", (E,), torch.int32, dev, optional=True),
+        _check(tracking, "tracking", (E,), torch.int64, dev, optional=True),
+    )
+    _rc(LIB.moe_layer_forward_noalloc(ctypes.byref(d), xp, ctypes.byref(W), *args,
+                                      _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def moe_residual_rmsnorm(d: MoeDesc, x_in, y, x_out, r_out, eps: float = 1e-6, stream=None):

@@ -8,6 +8,7 @@
 
 #include "backward.h"
 #include "kernels.h"
+#include "layer_check.h"
 
 namespace {
 
@@ -386,10 +387,13 @@ int moe_experts(const moe_desc_t* desc, const void* x, const float* topk_w,
 
 }  // extern "C"
 
-static int layer_forward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
-                         void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
-                         int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
-                         hipStream_t stream, const moe::StageTimer* tm) {
+namespace moe {
+
+int validate_desc(const moe_desc_t* desc) { return validate(desc); }
+
+int layer_forward_check(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                        void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                        int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes) {
   int rc = validate(desc);
   if (rc) return rc;
   if (desc->T == 0) return MOE_OK;
@@ -399,6 +403,18 @@ static int layer_forward(const moe_desc_t* desc, const void* x, const moe_weight
   const void* ps[] = {x, y, topk_idx_out, topk_w_out, logits_out, counts_out, tracking};
   for (const void* p : ps)
     if (misaligned(p)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+static int layer_forward(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                         void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
+                         int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
+                         hipStream_t stream, const moe::StageTimer* tm) {
+  int rc = moe::layer_forward_check(desc, x, weights, y, topk_idx_out, topk_w_out, logits_out,
+                                    counts_out, tracking, ws, ws_bytes);
+  if (rc || desc->T == 0) return rc;
   const moe_desc_t& d = *desc;
   const Layout L = make_layout(d);
   float* lg = (d.flags & MOE_F_WRITE_LOGITS) ? logits_out : nullptr;
@@ -519,6 +535,9 @@ const char* moe_strerror(int code) {
     case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_size()";
     case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case MOE_ERR_HIP: return "a HIP launch or runtime call failed";
+    case MOE_ERR_SCRATCH:
+      return "the layer needs more scratch than the no-allocation entry point's static buffer "
+             "holds (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

@@ -57,6 +57,8 @@ extern "C" {
 #define MOE_ERR_WORKSPACE (-3)   /* ws is NULL or ws_bytes < moe_workspace_size(desc) */
 #define MOE_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
 #define MOE_ERR_HIP (-5)         /* a HIP call failed; moe_strerror gives no HIP code */
+#define MOE_ERR_SCRATCH (-6)     /* moe_layer_forward_noalloc: the layer needs more scratch than
+                                    MOE_NOALLOC_SCRATCH_BYTES */
 
 /* ---- dtypes and flags ---------------------------------------------------- */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
@@ -161,6 +163,29 @@ int moe_layer_forward(const moe_desc_t* desc, const void* x, const moe_weights_t
                       void* y, int32_t* topk_idx_out, float* topk_w_out, float* logits_out,
                       int32_t* counts_out, int64_t* tracking, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer forward as moe_layer_forward (the same kernels, bit-identical
+ * results), with its workspace in a static buffer of the library instead of a
+ * caller's `ws`.  The buffer is MOE_NOALLOC_SCRATCH_BYTES of device memory per
+ * GPU, reserved by each GPU the library runs on until the process ends (it
+ * holds the full-size layer, H 2048, I 512, at up to 512 tokens).  Nothing is
+ * allocated: the first call on a device looks up that device's buffer address
+ * once (the call's current device must be the stream's), and every call
+ * clears the buffer's status word with a kernel before the layer's kernels.
+ * All calls on one GPU share its buffer: calls that overlap in time on one GPU
+ * (on different streams, or from different host threads) race and give
+ * undefined results; serialise them.
+ * Errors, on the host before anything is enqueued: those of moe_layer_forward
+ * (a workspace error cannot occur); MOE_ERR_SCRATCH when
+ * moe_workspace_size(desc) > MOE_NOALLOC_SCRATCH_BYTES; MOE_ERR_UNSUPPORTED
+ * with MOE_F_CHECK_FINITE (the status word is not readable from outside). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_forward_noalloc(const moe_desc_t* desc, const void* x, const moe_weights_t* weights,
+                              void* y, int32_t* topk_idx_out, float* topk_w_out,
+                              float* logits_out, int32_t* counts_out, int64_t* tracking,
+                              hipStream_t stream);
 
 /* Residual + RMSNorm for stacking layers (not on the pages; gamma = 1):
  *   x_out = RN(x_in + y)        (skipped, x_out = x_in, when y == NULL)

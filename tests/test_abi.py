@@ -131,8 +131,35 @@ def test_zero_tokens_is_a_noop(L):
                                    None) == 0
 
 
+def test_noalloc_host_errors(L):
+    """moe_layer_forward_noalloc rejects, on the host and before any device
+    call, a desc whose workspace exceeds its static buffer, the non-finite
+    check flag (its status word is not readable), and invalid descs; T = 0
+    is a no-op."""
+    big = full_desc(L, T=4096)
+    assert L.LIB.moe_workspace_size(ctypes.byref(big)) > L.MOE_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x100000)
+    W = L.MoeWeights(fake, None, fake, fake, fake, fake, fake, fake)
+    y = ctypes.c_void_p(0x200000)
+    rc = L.LIB.moe_layer_forward_noalloc(ctypes.byref(big), fake, ctypes.byref(W), y, None, None,
+                                         None, None, None, None)
+    assert rc == L.MOE_ERR_SCRATCH == -6
+    fits = full_desc(L, T=512)
+    assert L.LIB.moe_workspace_size(ctypes.byref(fits)) <= L.MOE_NOALLOC_SCRATCH_BYTES
+    fits.flags = L.MOE_F_CHECK_FINITE
+    assert L.LIB.moe_layer_forward_noalloc(ctypes.byref(fits), fake, ctypes.byref(W), y, None,
+                                           None, None, None, None, None) == -2
+    bad = full_desc(L, E=255)
+    assert L.LIB.moe_layer_forward_noalloc(ctypes.byref(bad), fake, ctypes.byref(W), y, None,
+                                           None, None, None, None, None) == -1
+    zero = full_desc(L, T=0)
+    assert L.LIB.moe_layer_forward_noalloc(ctypes.byref(zero), None, None, None, None, None, None,
+                                           None, None, None) == 0
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in L.strerror(-6)
+
+
 def test_strerror(L):
-    for c in [0, -1, -2, -3, -4, -5, 99]:
+    for c in [0, -1, -2, -3, -4, -5, -6, 99]:
         assert isinstance(L.strerror(c), str) and L.strerror(c)
     assert L.strerror(-3).startswith("workspace")
 
