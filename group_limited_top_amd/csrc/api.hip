@@ -13,6 +13,9 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+// Token counts stay below 2^30 so that every token index and launch-size
+// expression (token + block size, token + loop stride) fits an int.
+constexpr int32_t kMaxTokens = 1 << 30;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace regions (byte offsets from ws).  One layout serves every entry
@@ -100,6 +103,7 @@ int validate(const moe_desc_t* d) {
   if (d->I % 64 != 0 || d->I > 1024) return MOE_ERR_UNSUPPORTED;
   if (d->I_shared % 64 != 0 || d->I_shared > 1024) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->T * d->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (d->T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -493,7 +497,7 @@ int moe_sigmoid32(const float* z, float* s, int64_t n, hipStream_t stream) {
 }
 
 size_t moe_aux_loss_workspace_size(int32_t T, int32_t E) {
-  if (T < 1 || E < 2 || E > 1024) return 0;
+  if (T < 1 || T >= kMaxTokens || E < 2 || E > 1024) return 0;
   return align_up(moe::aux_workspace_bytes(T, E));
 }
 
@@ -518,7 +522,7 @@ int moe_bias_update(int32_t E, const int32_t* counts, const float* bias_in, floa
 int moe_aux_loss(int32_t T, int32_t E, const float* logits, const int32_t* counts, double* f,
                  double* P, double* loss, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 1 || E < 2 || !logits || !counts || !f || !P || !loss) return MOE_ERR_INVALID;
-  if (E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (E > 1024 || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < moe_aux_loss_workspace_size(T, E)) return MOE_ERR_WORKSPACE;
   const void* ps[] = {logits, counts, f, P, loss, ws};
   for (const void* p : ps)

@@ -223,8 +223,8 @@ constexpr int aux_waves() {  // waves per pass-1 block: LDS of NW * EPL * 64 dou
 int aux_blocks(int T, int E) {
   const int epl = (E + 63) / 64;
   const int nw = epl <= 4 ? aux_waves<4>() : (epl <= 8 ? aux_waves<8>() : aux_waves<16>());
-  const int b = (T + nw * kAuxTok - 1) / (nw * kAuxTok);
-  return b < 1 ? 1 : (b > kAuxMaxBlocks ? kAuxMaxBlocks : b);
+  const int64_t b = ((int64_t)T + nw * kAuxTok - 1) / (nw * kAuxTok);
+  return b < 1 ? 1 : (b > kAuxMaxBlocks ? kAuxMaxBlocks : (int)b);
 }
 
 template <int EPL>

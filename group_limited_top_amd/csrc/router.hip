@@ -257,8 +257,8 @@ bool logits_split_in_kernel(int T) { return T <= 1024; }
 static int logits_bm(int T) { return 64 * (logits_split_in_kernel(T) ? kLgMTSmall : kLgMTLarge); }
 
 int logits_ksplit(int T, int H, int E) {
-  const int bm = logits_bm(T);
-  const int tiles = ((T + bm - 1) / bm) * ((E + kLgBN - 1) / kLgBN);
+  const int64_t bm = logits_bm(T);
+  const int64_t tiles = ((T + bm - 1) / bm) * ((E + kLgBN - 1) / kLgBN);
   int ks = 1;
   while (ks < kMaxKSplit && tiles * ks * 2 <= 512 && (H / kLgKC) % (ks * 2) == 0) ks *= 2;
   return ks;
@@ -267,7 +267,7 @@ int logits_ksplit(int T, int H, int E) {
 hipError_t launch_logits_bf16(const uint16_t* x, const float* w32, const uint16_t* wsplit,
                               float* out, int T, int H, int E, int ks, hipStream_t s,
                               const StageTimer* tm) {
-  const int bm = logits_bm(T);
+  const int64_t bm = logits_bm(T);
   dim3 grid((unsigned)((T + bm - 1) / bm), (unsigned)((E + kLgBN - 1) / kLgBN), (unsigned)ks);
   const int KR = H / ks;
   stage_begin(tm, kLogits, s);

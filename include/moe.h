@@ -80,7 +80,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * group size E/n_group >= 2; n_group <= 64; 1 <= top_k <= 16;
  * top_k <= topk_group * E / n_group; H % 256 == 0 (bf16) or H % 64 == 0 and
  * H <= 16384 (fp32); I and I_shared multiples of 64 and at most 1024;
- * T * top_k < 2^31. */
+ * T < 2^30 and T * top_k < 2^31. */
 typedef struct {
   int32_t T;                   /* tokens */
   int32_t H;                   /* hidden size */
@@ -276,7 +276,7 @@ int moe_bias_update(int32_t E, const int32_t* counts, const float* bias_in, floa
                     double rate, hipStream_t stream);
 
 /* Bytes of device workspace moe_aux_loss needs for T tokens and E experts
- * (0 if T < 1, E < 2 or E > 1024).  Host only. */
+ * (0 if T < 1, T >= 2^30, E < 2 or E > 1024).  Host only. */
 size_t moe_aux_loss_workspace_size(int32_t T, int32_t E);
 
 /* Auxiliary load-balancing loss ([Pitfalls, MoE 负载均衡 Loss 别忘加]) from the
@@ -290,7 +290,7 @@ size_t moe_aux_loss_workspace_size(int32_t T, int32_t E);
  * f is exact; P and loss carry fp64 rounding of the exponentials and of sums
  * taken in a fixed order (bit-reproducible).  A non-finite logit makes the
  * results non-finite.  MOE_ERR_INVALID: T < 1, E < 2, a null pointer;
- * MOE_ERR_UNSUPPORTED: E > 1024; MOE_ERR_WORKSPACE: ws too small. */
+ * MOE_ERR_UNSUPPORTED: E > 1024 or T >= 2^30; MOE_ERR_WORKSPACE: ws too small. */
 int moe_aux_loss(int32_t T, int32_t E, const float* logits, const int32_t* counts, double* f,
                  double* P, double* loss, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -731,7 +731,7 @@ def test_stack19_t8k():
     # the step-by-step run ends where the stack did
     np.testing.assert_array_equal(nb(xg)[free], x_final)
     say("stack: sampled tokens with identical routing at all layers", int(agree.sum()), "/", n_s)
-    assert agree.sum() >= 16
+    assert agree.sum() >= 32  # 63 of 256 agreed when this bar was set
     got = oracle.bf16_bits_to_f32(x_final).astype(np.float64)
     ref = oracle.bf16_bits_to_f32(xo).astype(np.float64)
     r_end = rel_l2(got[agree], ref[agree])
