@@ -666,7 +666,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="full_t512")
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: the 512-token headline plus the "
+                         "16384- and 65536-token layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time steps launched one by one instead of a HIP graph of K steps")
@@ -688,8 +690,8 @@ def main():
     ap.add_argument("--profile-note", default="", help="with --write-traffic: the summary file")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(args.workload, *args.write_traffic, args.copy_calibration or 1024,
-                      args.profile_note)
+        write_traffic(args.workload or "full_t512", *args.write_traffic,
+                      args.copy_calibration or 1024, args.profile_note)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this layer's data-parallel share needs no "
@@ -710,7 +712,7 @@ def main():
     from group_limited_top_amd import _lib as L
     from group_limited_top_amd import synth
 
-    shape = synth.WORKLOADS[args.workload]
+    shape = synth.WORKLOADS[args.workload or "full_t512"]
     torch.cuda.set_device(0)
     if shape.layers != 1:
         print(json.dumps(bench_stack(L, shape, min(args.steps, 10), min(args.warmup, 2))), flush=True)
@@ -728,7 +730,7 @@ def main():
                       backward=not args.no_backward, cpu=not args.no_cpu_baseline,
                       cpu_tokens=args.cpu_tokens, peaks=peaks)
     out["peaks_measured"] = peaks
-    if args.workload == "full_t512" and not args.no_extra_workloads:
+    if args.workload is None and not args.no_extra_workloads:
         for key, name in EXTRA_WORKLOADS:
             out[key] = bench_layer(L, synth.WORKLOADS[name], min(args.steps, 20),
                                    min(args.warmup, 5), eager=args.eager, balance=False,
