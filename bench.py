@@ -502,7 +502,7 @@ def bench_backward(L, d, shape, xd, weights, K):
 
 
 TARGETS = {  # the layer fraction each regime is held to
-    "hbm": ("layer_hbm_frac", 0.60),
+    "hbm": ("layer_hbm_frac", 0.65),
     "mfma": ("layer_mfma_frac", 0.50),
 }
 

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void k_down_bf16(const ExpertArgs a, int hslic
 #pragma unroll
     for (int n = 0; n < kSub; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 va[8], vb[8], am[8];
+  u32x4 va[8], vb[8], vc[8], am[8];
   auto load = [&](u32x4 (&v)[8], int k0) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) v[r] = ld16_stream(wd + (size_t)(k0 + r) * H);
@@ -257,13 +257,18 @@ __global__ __launch_bounds__(256) void k_down_bf16(const ExpertArgs a, int hslic
       }
     }
   };
+  // three 32-deep batches rotate: two are in flight while one is used
   load(va, 0);
-  for (int k0 = 0; k0 < I; k0 += 64) {
-    if (k0 + 32 < I) load(vb, k0 + 32);
+  if (32 < I) load(vb, 32);
+  for (int k0 = 0; k0 < I; k0 += 96) {
+    if (k0 + 64 < I) load(vc, k0 + 64);
     step(va, k0);
     if (k0 + 32 >= I) break;
-    if (k0 + 64 < I) load(va, k0 + 64);
+    if (k0 + 96 < I) load(va, k0 + 96);
     step(vb, k0 + 32);
+    if (k0 + 64 >= I) break;
+    if (k0 + 128 < I) load(vb, k0 + 128);
+    step(vc, k0 + 64);
   }
 
   // epilogue: tile j, C row 4q+i -> h = h0 + 8*(4q+i) + j; 8 consecutive h per (n, i)
@@ -290,50 +295,67 @@ __global__ __launch_bounds__(256) void k_down_bf16(const ExpertArgs a, int hslic
 // in j order, fp32, one rounding.  [Routing §四] (weighted sum), §五 (shared
 // output added as is).
 // ----------------------------------------------------------------------------
+// KT > 0: top_k == KT known at compile time (fewer registers: more waves in
+// flight); KT == 0: any top_k <= 16.  A block takes NT consecutive tokens;
+// each thread one 16-byte chunk of all their rows, every row load issued
+// before any arithmetic.
+template <int KT, int NT>
 __global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
-  constexpr int kMaxK = 16;  // top_k <= 16 (the supported envelope)
-  const int t = blockIdx.x;
-  const int H = a.H, K = a.K;
+  constexpr int kMaxK = KT > 0 ? KT : 16;  // top_k <= 16 (the supported envelope)
+  const int K = KT > 0 ? KT : a.K;
+  const int H = a.H, T = a.T;
+  const int t0 = blockIdx.x * NT;
   const uint16_t* osh = reinterpret_cast<const uint16_t*>(a.o_shared);
   const uint16_t* orr = reinterpret_cast<const uint16_t*>(a.o_routed);
   uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
-  // the token's pair slots and weights, then every row load before any use,
-  // so that the K + 1 loads are in flight together
-  int32_t slot[kMaxK];
-  float wj[kMaxK];
+  int32_t slot[NT][kMaxK];
+  float wj[NT][kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;
-    wj[j] = j < K ? a.topk_w[(size_t)t * K + j] : 0.0f;
+  for (int u = 0; u < NT; ++u) {
+    const int t = min(t0 + u, T - 1);  // a token past the end repeats the last (not stored)
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      slot[u][j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;
+      wj[u][j] = j < K ? a.topk_w[(size_t)t * K + j] : 0.0f;
+    }
   }
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
-    const u32x4 vs = a.Is > 0 ? ld16(osh + (size_t)t * H + c * 8) : zero4;
-    u32x4 v[kMaxK];
+    u32x4 vs[NT], v[NT][kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) v[j] = slot[j] >= 0 ? ld16(orr + (size_t)slot[j] * H + c * 8) : zero4;
-    float acc[8];
+    for (int u = 0; u < NT; ++u) {
+      const int t = min(t0 + u, T - 1);
+      vs[u] = a.Is > 0 ? ld16(osh + (size_t)t * H + c * 8) : zero4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = bf16_lo(vs[i]);
-      acc[2 * i + 1] = bf16_hi(vs[i]);
+      for (int j = 0; j < kMaxK; ++j)
+        v[u][j] = slot[u][j] >= 0 ? ld16(orr + (size_t)slot[u][j] * H + c * 8) : zero4;
     }
-    // j order, one product and one sum per term, as specified
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (slot[j] < 0) continue;
+    for (int u = 0; u < NT; ++u) {
+      if (t0 + u >= T) break;  // block-uniform
+      float acc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = acc[2 * i] + wj[j] * bf16_lo(v[j][i]);
-        acc[2 * i + 1] = acc[2 * i + 1] + wj[j] * bf16_hi(v[j][i]);
+        acc[2 * i] = bf16_lo(vs[u][i]);
+        acc[2 * i + 1] = bf16_hi(vs[u][i]);
       }
+      // j order, one product and one sum per term, as specified
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (slot[u][j] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = acc[2 * i] + wj[u][j] * bf16_lo(v[u][j][i]);
+          acc[2 * i + 1] = acc[2 * i + 1] + wj[u][j] * bf16_hi(v[u][j][i]);
+        }
+      }
+      u32x4 pk;
+      pk.x = pack_bf16x2(acc[0], acc[1]);
+      pk.y = pack_bf16x2(acc[2], acc[3]);
+      pk.z = pack_bf16x2(acc[4], acc[5]);
+      pk.w = pack_bf16x2(acc[6], acc[7]);
+      st16(y + (size_t)(t0 + u) * H + c * 8, pk);
     }
-    u32x4 pk;
-    pk.x = pack_bf16x2(acc[0], acc[1]);
-    pk.y = pack_bf16x2(acc[2], acc[3]);
-    pk.z = pack_bf16x2(acc[4], acc[5]);
-    pk.w = pack_bf16x2(acc[6], acc[7]);
-    st16(y + (size_t)t * H + c * 8, pk);
   }
 }
 
@@ -360,13 +382,19 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTi
     hipLaunchKernelGGL(k_gateup_bf16, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
     stage_end(tm, kGateUp, s);
   }
-  const int hslices = (a.H + 511) / 512;
-  const size_t lds = (size_t)kTileRows * (imax / 8 + 1) * 16;
-  stage_begin(tm, kDown, s);
-  hipLaunchKernelGGL(k_down_bf16, dim3((unsigned)(tiles * hslices)), dim3(256), lds, s, a, hslices);
-  stage_end(tm, kDown, s);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (down_stream_ok(a)) {
+    const hipError_t e = launch_down_stream_bf16(a, tiles, s, tm);
+    if (e != hipSuccess) return e;
+  } else {
+    const int hslices = (a.H + 511) / 512;
+    const size_t lds = (size_t)kTileRows * (imax / 8 + 1) * 16;
+    stage_begin(tm, kDown, s);
+    hipLaunchKernelGGL(k_down_bf16, dim3((unsigned)(tiles * hslices)), dim3(256), lds, s, a,
+                       hslices);
+    stage_end(tm, kDown, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_combine_bf16(a, s, tm);
 }
 
@@ -387,15 +415,25 @@ const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int I
       return stream_ring_ok(a) ? "k_gateup_stream" : "k_gateup_bf16";
     case kDown:
       if (!bf16) return "k_down_f32";
-      return tiled ? "k_expert_gemm<1>" : "k_down_bf16";
+      if (tiled) return "k_expert_gemm<1>";
+      return down_stream_ok(a) ? "k_down_stream" : "k_down_bf16";
     case kCombine: return bf16 ? "k_combine_bf16" : "k_combine_f32";
     default: return nullptr;
   }
 }
 
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
 hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
   stage_begin(tm, kCombine, s);
-  hipLaunchKernelGGL(k_combine_bf16, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  if (a.K == 8) {
+    constexpr int NT = MOE_COMBINE_NT;
+    hipLaunchKernelGGL((k_combine_bf16<8, NT>), dim3((unsigned)((a.T + NT - 1) / NT)), dim3(256), 0,
+                       s, a);
+  } else {
+    hipLaunchKernelGGL((k_combine_bf16<0, 1>), dim3((unsigned)a.T), dim3(256), 0, s, a);
+  }
   stage_end(tm, kCombine, s);
   return hipGetLastError();
 }

@@ -83,6 +83,10 @@ hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const St
 bool stream_ring_ok(const ExpertArgs& a);
 hipError_t launch_gateup_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,
                                      const StageTimer* tm);
+// down weight streaming through the same ring; usable when down_stream_ok.
+bool down_stream_ok(const ExpertArgs& a);
+hipError_t launch_down_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,
+                                   const StageTimer* tm);
 hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm = nullptr);
 hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTimer* tm = nullptr);
