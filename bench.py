@@ -40,16 +40,17 @@ def algorithmic_work(shape, counts):
     Bytes count what the method must move at least once: the weights of every
     expert that received a token, the shared expert, the router weight, x, y
     and the routing outputs.  Intermediates (hidden activations, per-pair
-    outputs) are excluded from the layer figure; the kernel figures count the
-    kernel's own inputs and outputs once."""
+    outputs) are excluded everywhere: the gate/up figure (the roofline's
+    dominant kernel at small T) is its weights and x, the down figure its
+    weights only."""
     T, H, I, Is, K, E = shape.T, shape.H, shape.I, shape.I_shared, shape.top_k, shape.E
     elt = 2 if shape.dtype == "bf16" else 4
     hit = int((counts > 0).sum())
     P = T * K
     gate_up_w = (hit * 2 * I * H + 2 * Is * H) * elt
     down_w = (hit * I * H + Is * H) * elt
-    k_gate_up = gate_up_w + T * H * elt + (P * I + T * Is) * elt
-    k_down = down_w + (P * I + T * Is) * elt + (P + (T if Is else 0)) * H * elt
+    k_gate_up = gate_up_w + T * H * elt
+    k_down = down_w
     layer = (gate_up_w + down_w + E * H * 4 + 2 * T * H * elt + P * 8)
     flops_gate_up = 2.0 * 2 * (P * I + T * Is) * H
     flops_down = 2.0 * (P * I + T * Is) * H
