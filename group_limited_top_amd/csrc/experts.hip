@@ -410,11 +410,11 @@ const char* expert_stage_kernel(int stage, int64_t T, int K, int E, int I, int I
   a.Is = Is;
   switch (stage) {
     case kGateUp:
-      if (!bf16) return "k_gateup_f32";
+      if (!bf16) return stream_f32_ok(a) ? "k_gateup_stream_f32" : "k_gateup_f32";
       if (tiled) return "k_expert_gemm<0>";
       return stream_ring_ok(a) ? "k_gateup_stream" : "k_gateup_bf16";
     case kDown:
-      if (!bf16) return "k_down_f32";
+      if (!bf16) return stream_f32_ok(a) ? "k_down_stream_f32" : "k_down_f32";
       if (tiled) return "k_expert_gemm<1>";
       return down_stream_ok(a) ? "k_down_stream" : "k_down_bf16";
     case kCombine: return bf16 ? "k_combine_bf16" : "k_combine_f32";
@@ -697,15 +697,20 @@ hipError_t launch_experts_f32(const ExpertArgs& a, hipStream_t s, const StageTim
     stage_end(tm, kTiles, s);
   }
   const int64_t tiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
-  const int imax = a.I > a.Is ? a.I : a.Is;
-  const int slices = imax / 64;
-  stage_begin(tm, kGateUp, s);
-  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
-  stage_end(tm, kGateUp, s);
-  const int hslices = (a.H + 511) / 512;
-  stage_begin(tm, kDown, s);
-  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(256), 0, s, a, hslices);
-  stage_end(tm, kDown, s);
+  if (stream_f32_ok(a)) {
+    const hipError_t e = launch_stream_f32(a, tiles, s, tm);
+    if (e != hipSuccess) return e;
+  } else {
+    const int imax = a.I > a.Is ? a.I : a.Is;
+    const int slices = imax / 64;
+    stage_begin(tm, kGateUp, s);
+    hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)(tiles * slices)), dim3(256), 0, s, a, slices);
+    stage_end(tm, kGateUp, s);
+    const int hslices = (a.H + 511) / 512;
+    stage_begin(tm, kDown, s);
+    hipLaunchKernelGGL(k_down_f32, dim3((unsigned)(tiles * hslices)), dim3(256), 0, s, a, hslices);
+    stage_end(tm, kDown, s);
+  }
   stage_begin(tm, kCombine, s);
   hipLaunchKernelGGL(k_combine_f32, dim3((unsigned)a.T), dim3(256), 0, s, a);
   stage_end(tm, kCombine, s);

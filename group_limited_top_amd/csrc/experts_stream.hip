@@ -27,6 +27,8 @@
 // item into the next, so no block pays a ring fill or leaves a CU idle at the
 // end of the grid.
 
+#include <type_traits>
+
 #include "device.h"
 #include "expert_tiles.h"
 #include "kernels.h"
@@ -99,20 +101,41 @@ __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) {
   *(__attribute__((address_space(1))) u32x4*)p = v;
 }
 
-// Item t = tile t / S, slice t % S.  Stage rows 0..127: weight rows, 128..159:
-// token rows; load j of wave w covers stage rows 16 j + 4 w .. + 3 (16 lanes
-// per 256-byte row), so loads 0..7 bring weights and 8, 9 token rows.
-//   MODE 0: weight row r < 64 is gate row i0 + r, r >= 64 up row i0 + r - 64,
-//           at K columns 128 s .. of stage s; chunk c at sswz(r, c).
-//   MODE 1: weight row r is W_down row (k) 128 s + r at columns i0 .. i0 + 127;
-//           chunk c at r * 256 + 16 (c ^ wd_swz(r)), the layout the transpose
-//           read wants (16 rows read at one 32-byte window meet two to a
-//           window).
-// Token rows (both modes): chunk c of row 128 + n at sswz(128 + n, c).
+// fp32 down stages: W_down k-row r (512 bytes: 128 output columns) keeps
+// 16-byte chunk c at r * 512 + 16 (c ^ 4 ((r >> 2) & 3)), so the four k-rows
+// that one per-element operand read covers (4 apart) meet four different
+// 64-byte bank groups.
+__device__ __forceinline__ int f32d_chunk(int r, int c) { return c ^ (((r >> 2) & 3) << 2); }
+
+// Item t = tile t / S, slice t % S.  A stage is 160 KiB / 4 = 40 KiB: 32 KiB
+// of weight rows, then 32 token rows of 256 bytes (stage rows 128..159, chunk
+// c at sswz(128 + n, c)); loads 0..7 of each wave bring weights, 8 and 9
+// token rows (load j of wave w fills stage bytes 4096 j + 1024 w + 16 lane).
+//   MODE 0 (gate/up, bf16): weight row r < 64 is gate row i0 + r, r >= 64 up
+//     row i0 + r - 64, K columns 128 s .. of stage s (256 bytes); chunk c at
+//     sswz(r, c).
+//   MODE 1 (down, bf16): weight row r is W_down row (k) 128 s + r at columns
+//     i0 .. i0 + 127; chunk c at r * 256 + 16 (c ^ wd_swz(r)), the layout the
+//     transpose read wants (16 rows read at one 32-byte window meet two to a
+//     window).
+//   MODE 2 (gate/up, fp32): as MODE 0 with fp32 rows: K columns 64 s .. (256
+//     bytes), 64 features an item.
+//   MODE 3 (down, fp32): weight row r (of 64) is W_down row 64 s + r at
+//     columns i0 .. i0 + 127 (512 bytes), chunk c at r * 512 + 16
+//     f32d_chunk(r, c); token rows carry K columns 64 s ...
 template <int MODE>
 __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
-  constexpr int kLoads = 10;   // loads per wave per stage
-  constexpr int kStores = 2;   // epilogue stores per wave
+  constexpr bool kDown = (MODE & 1) != 0;
+  constexpr bool kF32 = MODE >= 2;
+  typedef typename std::conditional<kF32, float, uint16_t>::type elt_t;
+  constexpr int kEl = sizeof(elt_t);
+  constexpr int kSK = kF32 ? 64 : kSBK;  // K depth of a stage
+  constexpr int kCols = kDown ? kSOut : kSFeat;  // output columns (features) an item
+  constexpr int kLoads = 10;  // loads per wave per stage
+  constexpr int kStores = MODE == 3 ? 4 : 2;  // epilogue stores per wave
+  // with at least 4 stages an item the epilogue's item is one of the last two
+  // the issue cursor started (fp32 down items may have fewer: re-read)
+  constexpr bool kKeepItems = MODE != 3;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kStageB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,24 +144,25 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   // everything from the argument block is read here, before the first asm
   // statement (see k_expert_gemm)
   const uint8_t* const x_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.x));
-  const uint16_t* const wg_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_gate));
-  const uint16_t* const wu_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_up));
-  const ptrdiff_t sh_g = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_gate)) - wg_p;
-  const ptrdiff_t sh_u = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_up)) - wu_p;
-  const uint16_t* const wd_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_down));
-  const ptrdiff_t sh_d = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_down)) - wd_p;
+  const elt_t* const wg_p = uniform_ptr(reinterpret_cast<const elt_t*>(a.w_gate));
+  const elt_t* const wu_p = uniform_ptr(reinterpret_cast<const elt_t*>(a.w_up));
+  const ptrdiff_t sh_g = uniform_ptr(reinterpret_cast<const elt_t*>(a.ws_gate)) - wg_p;
+  const ptrdiff_t sh_u = uniform_ptr(reinterpret_cast<const elt_t*>(a.ws_up)) - wu_p;
+  const elt_t* const wd_p = uniform_ptr(reinterpret_cast<const elt_t*>(a.w_down));
+  const ptrdiff_t sh_d = uniform_ptr(reinterpret_cast<const elt_t*>(a.ws_down)) - wd_p;
   const int32_t* const sp_p = uniform_ptr(a.sorted_pair);
-  uint16_t* const hr_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.h_routed));
-  const ptrdiff_t sh_h = uniform_ptr(reinterpret_cast<uint16_t*>(a.h_shared)) - hr_p;
-  uint16_t* const or_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.o_routed));
-  const ptrdiff_t sh_o = uniform_ptr(reinterpret_cast<uint16_t*>(a.o_shared)) - or_p;
+  elt_t* const hr_p = uniform_ptr(reinterpret_cast<elt_t*>(a.h_routed));
+  const ptrdiff_t sh_h = uniform_ptr(reinterpret_cast<elt_t*>(a.h_shared)) - hr_p;
+  elt_t* const or_p = uniform_ptr(reinterpret_cast<elt_t*>(a.o_routed));
+  const ptrdiff_t sh_o = uniform_ptr(reinterpret_cast<elt_t*>(a.o_shared)) - or_p;
   const int32_t* const tab_p = uniform_ptr(a.tile_tab);
   const int32_t* const toff_p = uniform_ptr(a.tile_off);
   // dropped stores (rows past a tile's end) go to the padding rows of
-  // h_routed, which nothing reads: 8 (MODE 0) or 16 (MODE 1) bytes a lane,
-  // at most 32 KiB past the last row (the padding holds kGRows rows of I >= 64)
-  uint16_t* const trash = hr_p + (size_t)T * K * I + (size_t)(blockIdx.x & 7) * 2048 +
-                          (MODE == 0 ? 4 : 8) * tid;
+  // h_routed, which nothing reads: 8 (MODE 0) or 16 bytes a lane, at most
+  // 32 KiB past the last row (the padding holds kGRows rows of I >= 64)
+  elt_t* const trash = hr_p + (size_t)T * K * I +
+                       (kF32 ? (size_t)(blockIdx.x & 7) * 1024 + 4 * tid
+                             : (size_t)(blockIdx.x & 7) * 2048 + (MODE == 0 ? 4 : 8) * tid);
 
   // this block's items: first + m * nbx, m = 0 .. count - 1 (XCD x, i.e.
   // blocks b with b mod 8 = x, takes the x-th eighth of the list, so the
@@ -150,8 +174,8 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   const int first = lo + (int)(blockIdx.x >> 3);
   if (first >= hi) return;
   const int count = (hi - first + nbx - 1) / nbx;
-  const int nst = (MODE == 0 ? H : I) / kSBK;  // stages per item
-  const int total = count * nst;                // stages of this block
+  const int nst = (kDown ? I : H) / kSK;  // stages per item
+  const int total = count * nst;          // stages of this block
   auto item = [&](int m) __attribute__((always_inline)) {
     const int t = __builtin_amdgcn_readfirstlane(first + m * nbx);
     const int rt = t / S;
@@ -160,20 +184,25 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
     it.e = v & 0xffff;
     it.nrows = v >> 16;
     it.row0 = __builtin_amdgcn_readfirstlane(sload(tab_p + 2 * rt + 1));
-    it.i0 = (t - rt * S) * (MODE == 0 ? kSFeat : kSOut);
+    it.i0 = (t - rt * S) * kCols;
     return it;
   };
-  // lane offsets of the weight loads (fixed; MODE 0: row (r & 63) of the
-  // item's 64 of gate or up, MODE 1: row r of the stage's 128) and of the
-  // token loads (per item)
+  // lane offsets of the weight loads (fixed; gate/up: row (r & 63) of the
+  // item's 64 of gate or up; down: row r of the stage) and of the token
+  // loads (per item)
   uint32_t off[10];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = 16 * j + 4 * w + (lane >> 4);
-    off[j] = MODE == 0 ? (uint32_t)((r & 63) * H * 2 + (((lane & 15) ^ (r & 15)) << 4))
-                       : (uint32_t)(r * H * 2 + (((lane & 15) ^ wd_swz(r)) << 4));
+    if (MODE == 3) {
+      const int r = 8 * j + 2 * w + (lane >> 5);
+      off[j] = (uint32_t)(r * H * 4 + (f32d_chunk(r, lane & 31) << 4));
+    } else {
+      const int r = 16 * j + 4 * w + (lane >> 4);
+      off[j] = kDown ? (uint32_t)(r * H * 2 + (((lane & 15) ^ wd_swz(r)) << 4))
+                     : (uint32_t)((r & 63) * H * kEl + (((lane & 15) ^ (r & 15)) << 4));
+    }
   }
-  int32_t ptok[2];  // MODE 0: sorted pairs of the token rows of the next item (gathered)
+  int32_t ptok[2];  // gate/up: sorted pairs of the token rows of the next item (gathered)
   int pe = 0;
   auto fetch_rows = [&](int m) __attribute__((always_inline)) {
     const GItem it = item(m);
@@ -193,7 +222,7 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
       ptok[j] = v;
     }
   };
-  if (MODE == 0) fetch_rows(0);
+  if (!kDown) fetch_rows(0);
 
   // stage cursor: item sm, stage sk of it; prev and cur are the last two
   // items started (the epilogue's, kept so that it reads no table entry)
@@ -207,7 +236,7 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
       prev = cur;
       cur = it;
       const bool sh = it.e >= E;
-      if (MODE == 0) {
+      if (!kDown) {
         const size_t wofs = (sh ? 0 : (size_t)it.e * I * H) + (size_t)it.i0 * H;
         gb = reinterpret_cast<const uint8_t*>(uniform_ptr(wg_p + (sh ? sh_g : 0) + wofs));
         ub = reinterpret_cast<const uint8_t*>(uniform_ptr(wu_p + (sh ? sh_u : 0) + wofs));
@@ -216,7 +245,7 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
         for (int j = 0; j < 2; ++j) {
           const int r = 16 * (8 + j) + 4 * w + (lane >> 4);
           const int tok = pe < E ? ptok[j] / K : ptok[j];
-          off[8 + j] = (uint32_t)(min(tok, T - 1) * H * 2 + (((lane & 15) ^ (r & 15)) << 4));
+          off[8 + j] = (uint32_t)(min(tok, T - 1) * H * kEl + (((lane & 15) ^ (r & 15)) << 4));
         }
         if (sm + 1 < count) fetch_rows(sm + 1);
       } else {
@@ -229,13 +258,15 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
         for (int j = 0; j < 2; ++j) {
           const int r = 16 * (8 + j) + 4 * w + (lane >> 4);
           const int tr = min(r - 128, it.nrows - 1);
-          off[8 + j] = (uint32_t)(tr * I * 2 + (((lane & 15) ^ (r & 15)) << 4));
+          off[8 + j] = (uint32_t)(tr * I * kEl + (((lane & 15) ^ (r & 15)) << 4));
         }
       }
     }
     const void* base[10] = {gb, gb, gb, gb, ub, ub, ub, ub, tb, tb};
     const uint32_t lds = ring0_of(ring, c & 3, w);
-    const size_t kw = MODE == 0 ? (size_t)sk * kSRowB : (size_t)sk * kSBK * H * 2;
+    // stage advance: gate/up weights and all token rows move 256 bytes along
+    // K; down weights move kSK rows
+    const size_t kw = kDown ? (size_t)sk * kSK * H * kEl : (size_t)sk * kSRowB;
     const int kt = sk * kSRowB;
     const void* bk[10];
 #pragma unroll
@@ -245,8 +276,8 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
     if (++sk == nst) sk = 0;
   };
 
-  // MODE 0: acc[0][n] gate, acc[1][n] up, features 16 w + (MFMA row) of token
-  // tile n.  MODE 1: acc[t][n], column tile t (see below), token tile n.
+  // acc[t][n]: gate/up: t = 0 gate, 1 up, features 16 w + (MFMA row) of
+  // token tile n; down: column tile t (see below), token tile n
   f32x4 acc[2][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -260,59 +291,118 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   // share their swizzle.
   const int dn_lane =
       (8 * q + (r16 >> 2)) * kSRowB + (((4 * w + (r16 & 3)) ^ wd_swz(8 * q + (r16 >> 2))) << 4);
+  // fp32 (16x16x4 MFMA, one element of A and of B a lane): K block b of 16
+  // is read as 16-byte chunks 4 b + q (k = 16 b + 4 q .. + 3) and MFMA j of
+  // the block takes element j, i.e. k = 16 b + 4 q + j from lane group q.
+  // MODE 3's A operand (W_down[k][column]) is read element by element: lane
+  // (m, q) takes k row 16 b + 4 q + j at column 32 w + 16 t + m.
   auto compute = [&](int c) __attribute__((always_inline)) {
     const uint8_t* st = ring + (c & 3) * kStageB;
-    u32x4 A0[4], A1[4], B[4][2];
+    if (!kF32) {
+      u32x4 A0[4], A1[4], B[4][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (MODE == 0) {
-        A0[u] = lds16(st + sswz(16 * w + r16, 4 * u + q));
-        A1[u] = lds16(st + sswz(64 + 16 * w + r16, 4 * u + q));
-      } else {
-        const uint8_t* p = st + 32 * u * kSRowB + dn_lane;
-        u32x2 l0 = lds_tr16(p), h0 = lds_tr16(p + 4 * kSRowB);
-        u32x2 l1 = lds_tr16(p + 8), h1 = lds_tr16(p + 8 + 4 * kSRowB);
-        A0[u] = u32x4{l0.x, l0.y, h0.x, h0.y};
-        A1[u] = u32x4{l1.x, l1.y, h1.x, h1.y};
+      for (int u = 0; u < 4; ++u) {
+        if (!kDown) {
+          A0[u] = lds16(st + sswz(16 * w + r16, 4 * u + q));
+          A1[u] = lds16(st + sswz(64 + 16 * w + r16, 4 * u + q));
+        } else {
+          const uint8_t* p = st + 32 * u * kSRowB + dn_lane;
+          u32x2 l0 = lds_tr16(p), h0 = lds_tr16(p + 4 * kSRowB);
+          u32x2 l1 = lds_tr16(p + 8), h1 = lds_tr16(p + 8 + 4 * kSRowB);
+          A0[u] = u32x4{l0.x, l0.y, h0.x, h0.y};
+          A1[u] = u32x4{l1.x, l1.y, h1.x, h1.y};
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) B[u][n] = lds16(st + sswz(128 + 16 * n + r16, 4 * u + q));
       }
 #pragma unroll
-      for (int n = 0; n < 2; ++n) B[u][n] = lds16(st + sswz(128 + 16 * n + r16, 4 * u + q));
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          acc[0][n] = mfma16x16x32(A0[u], B[u][n], acc[0][n]);
+          acc[1][n] = mfma16x16x32(A1[u], B[u][n], acc[1][n]);
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 B[2];
+        float A[2][4];  // [t][j]: the A element of MFMA j of operand t
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          B[n] = __builtin_bit_cast(f32x4, lds16(st + sswz(128 + 16 * n + r16, 4 * b + q)));
+        if (!kDown) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const f32x4 v =
+                __builtin_bit_cast(f32x4, lds16(st + sswz(64 * t + 16 * w + r16, 4 * b + q)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) A[t][j] = v[j];
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 16 * b + 4 * q + j, col = 32 * w + 16 * t + r16;
+              A[t][j] = *reinterpret_cast<const float*>(
+                  st + r * 512 + (f32d_chunk(r, col >> 2) << 4) + 4 * (col & 3));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[t][j], B[n][j], acc[t][n], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        acc[0][n] = mfma16x16x32(A0[u], B[u][n], acc[0][n]);
-        acc[1][n] = mfma16x16x32(A1[u], B[u][n], acc[1][n]);
-      }
   };
   // epilogue: exactly kStores stores per wave (rows past the tile end go to
   // trash).  MODE 0: lane holds features i0 + 16 w + 4 q + 0..3 of token row
-  // 16 n + r16; MODE 1: columns i0 + 32 w + 8 q + 0..7 of token row 16 n + r16.
+  // 16 n + r16 (bf16, 8 bytes); MODE 1: columns i0 + 32 w + 8 q + 0..7 (16
+  // bytes); MODE 2: features i0 + 16 w + 4 q + 0..3 (fp32, 16 bytes); MODE 3:
+  // columns i0 + 32 w + 16 t + 4 q + 0..3 of column tile t (fp32, 16 bytes).
   auto epilogue = [&](const GItem& it) __attribute__((always_inline)) {
     const bool sh = it.e >= E;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int row = 16 * n + r16;
-      if (MODE == 0) {
-        uint16_t* hb = hr_p + (sh ? sh_h : 0) + (size_t)it.row0 * I + it.i0 + 16 * w + 4 * q;
+      const bool ok = row < it.nrows;
+      if (MODE == 0 || MODE == 2) {
+        elt_t* hb = hr_p + (sh ? sh_h : 0) + (size_t)it.row0 * I + it.i0 + 16 * w + 4 * q;
         float hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hv[i] = silu_f32(acc[0][n][i]) * acc[1][n][i];
-        u32x2 pk;
-        pk.x = pack_bf16x2(hv[0], hv[1]);
-        pk.y = pack_bf16x2(hv[2], hv[3]);
-        store8(row < it.nrows ? hb + (size_t)row * I : trash, pk);
-      } else {
-        uint16_t* ob = or_p + (sh ? sh_o : 0) + (size_t)it.row0 * H + it.i0 + 32 * w + 8 * q;
+        if (MODE == 0) {
+          u32x2 pk;
+          pk.x = pack_bf16x2(hv[0], hv[1]);
+          pk.y = pack_bf16x2(hv[2], hv[3]);
+          store8(reinterpret_cast<uint16_t*>(ok ? hb + (size_t)row * I : trash), pk);
+        } else {
+          const u32x4 pk = {__float_as_uint(hv[0]), __float_as_uint(hv[1]),
+                            __float_as_uint(hv[2]), __float_as_uint(hv[3])};
+          store16(reinterpret_cast<uint16_t*>(ok ? hb + (size_t)row * I : trash), pk);
+        }
+      } else if (MODE == 1) {
+        elt_t* ob = or_p + (sh ? sh_o : 0) + (size_t)it.row0 * H + it.i0 + 32 * w + 8 * q;
         u32x4 pk;
         pk.x = pack_bf16x2(acc[0][n][0], acc[0][n][1]);
         pk.y = pack_bf16x2(acc[0][n][2], acc[0][n][3]);
         pk.z = pack_bf16x2(acc[1][n][0], acc[1][n][1]);
         pk.w = pack_bf16x2(acc[1][n][2], acc[1][n][3]);
-        store16(row < it.nrows ? ob + (size_t)row * H : trash, pk);
+        store16(reinterpret_cast<uint16_t*>(ok ? ob + (size_t)row * H : trash), pk);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          elt_t* ob = or_p + (sh ? sh_o : 0) + (size_t)it.row0 * H + it.i0 + 32 * w + 16 * t + 4 * q;
+          const u32x4 pk = {__float_as_uint(acc[t][n][0]), __float_as_uint(acc[t][n][1]),
+                            __float_as_uint(acc[t][n][2]), __float_as_uint(acc[t][n][3])};
+          store16(reinterpret_cast<uint16_t*>(ok ? ob + (size_t)row * H : trash), pk);
+        }
       }
-      acc[0][n] = acc[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
@@ -320,6 +410,8 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   // load stage c + 3 into c - 1's buffer, run the epilogue of the previous item
   // when c starts a new one (its stores are then younger than stage c + 3's
   // loads: the waits of stages c + 1 .. c + 3 leave them outstanding), compute.
+  // (A wait that may have two epilogues' stores outstanding, with fewer than
+  // 4 stages an item, counts one: it waits for more than it needs.)
   for (int c = 0; c < 3 && c < total; ++c) issue(c);
   int epi = -8;  // stage at which the last epilogue ran
   for (int c = 0; c < total; ++c) {
@@ -332,12 +424,14 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
     // (with nst >= 4 stages an item, issue(c + 3) has not started another
     // item yet: prev is item c / nst - 1)
     if (c > 0 && c % nst == 0) {
-      epilogue(prev);
+      if (kKeepItems) epilogue(prev);
+      else epilogue(item(c / nst - 1));
       epi = c;
     }
     compute(c);
   }
-  epilogue(cur);
+  if (kKeepItems) epilogue(cur);
+  else epilogue(item(count - 1));
 }
 
 __global__ __launch_bounds__(256, 1) void k_gateup_stream(const ExpertArgs a, int S) {
@@ -345,6 +439,12 @@ __global__ __launch_bounds__(256, 1) void k_gateup_stream(const ExpertArgs a, in
 }
 __global__ __launch_bounds__(256, 1) void k_down_stream(const ExpertArgs a, int S) {
   stream_body<1>(a, S);
+}
+__global__ __launch_bounds__(256, 1) void k_gateup_stream_f32(const ExpertArgs a, int S) {
+  stream_body<2>(a, S);
+}
+__global__ __launch_bounds__(256, 1) void k_down_stream_f32(const ExpertArgs a, int S) {
+  stream_body<3>(a, S);
 }
 
 bool stream_ring_ok(const ExpertArgs& a) {
@@ -376,6 +476,28 @@ hipError_t launch_gateup_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStre
   stage_begin(tm, kGateUp, s);
   hipLaunchKernelGGL(k_gateup_stream, stream_grid(tiles * slices), dim3(256), 0, s, a, slices);
   stage_end(tm, kGateUp, s);
+  return hipGetLastError();
+}
+
+bool stream_f32_ok(const ExpertArgs& a) {
+  // whole 64-deep stages, at least 4 an item for gate/up; 64-feature and
+  // 128-column slices; routed and shared experts of one width; lane offsets
+  // 32-bit
+  return a.H % 128 == 0 && a.H / 64 >= 4 && a.I % 64 == 0 && (a.Is == 0 || a.Is == a.I) &&
+         (int64_t)a.T * a.H * 4 < (int64_t(1) << 31) &&
+         (int64_t)64 * a.H * 4 < (int64_t(1) << 31) && (int64_t)kTileRows * a.I * 4 < (int64_t(1) << 31);
+}
+
+hipError_t launch_stream_f32(const ExpertArgs& a, int64_t tiles, hipStream_t s,
+                             const StageTimer* tm) {
+  const int gslices = a.I / kSFeat, dslices = a.H / kSOut;
+  stage_begin(tm, kGateUp, s);
+  hipLaunchKernelGGL(k_gateup_stream_f32, stream_grid(tiles * gslices), dim3(256), 0, s, a,
+                     gslices);
+  stage_end(tm, kGateUp, s);
+  stage_begin(tm, kDown, s);
+  hipLaunchKernelGGL(k_down_stream_f32, stream_grid(tiles * dslices), dim3(256), 0, s, a, dslices);
+  stage_end(tm, kDown, s);
   return hipGetLastError();
 }
 

@@ -85,6 +85,11 @@ hipError_t launch_gateup_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStre
                                      const StageTimer* tm);
 // down weight streaming through the same ring; usable when down_stream_ok.
 bool down_stream_ok(const ExpertArgs& a);
+// fp32 gate/up and down weight streaming through the same ring; usable when
+// stream_f32_ok.
+bool stream_f32_ok(const ExpertArgs& a);
+hipError_t launch_stream_f32(const ExpertArgs& a, int64_t tiles, hipStream_t s,
+                             const StageTimer* tm);
 hipError_t launch_down_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,
                                    const StageTimer* tm);
 hipError_t launch_combine_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
