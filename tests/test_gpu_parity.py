@@ -372,6 +372,56 @@ def test_experts_f32_shapes(T, H, I, Is, hot):
     assert row_rel(got, ref).max() <= 1e-5
 
 
+@pytest.mark.parametrize("T,H,I,Is,hot", [(300, 384, 192, 192, 0), (150, 256, 64, 64, 70),
+                                           (1000, 512, 128, 0, 200), (33, 1024, 256, 256, 0)])
+def test_experts_f32_stream_shapes(T, H, I, Is, hot):
+    """fp32 weight-streaming path (H a multiple of 128, I of 64, the shared
+    expert as wide as the routed ones): three gate/up slices (I = 192),
+    one-stage down items (I = 64), three down column slices (H = 384), no
+    shared expert, and `hot` tokens all choosing expert 3 (many 32-row
+    tiles of one expert, the last partial)."""
+    say("experts f32 stream", T, H, I, Is, hot)
+    shape = synth.small_shape(T, H=H, I=I, I_shared=Is, dtype="f32", seed=720 + T)
+    dev = make_layer(shape)
+    rng = np.random.default_rng(T + 3 * H)
+    idx, w = _random_routing(rng, T, shape.E, shape.top_k)
+    for t in range(hot):
+        if 3 not in idx[t]:
+            idx[t, 0] = 3
+    d = L().desc_from_shape(shape)
+    assert L().moe_stage_kernel(d, "gate_up") == "k_gateup_stream_f32"
+    assert L().moe_stage_kernel(d, "down") == "k_down_stream_f32"
+    y = _gpu_experts(d, dev, idx, w)
+    ref = oracle.experts(nb(dev["x"]), idx, w, *oracle_weights(dev))
+    got = to_f64(y)
+    assert rel_l2(got, ref) <= 5e-6
+    assert row_rel(got, ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("T,H,I,Is,hot", [(200, 1024, 640, 640, 0), (64, 512, 1024, 0, 0),
+                                           (300, 2048, 512, 0, 120)])
+def test_experts_bf16_stream_shapes(T, H, I, Is, hot):
+    """bf16 weight-streaming path at other widths: 5- and 8-stage down items
+    (I = 640, 1024), 4 and 8 down column slices (H = 512, 1024), no shared
+    expert, and a hot expert with several tiles."""
+    say("experts bf16 stream", T, H, I, Is, hot)
+    shape = synth.small_shape(T, H=H, I=I, I_shared=Is, dtype="bf16", seed=740 + T)
+    dev = make_layer(shape)
+    rng = np.random.default_rng(T + 5 * H)
+    idx, w = _random_routing(rng, T, shape.E, shape.top_k)
+    for t in range(hot):
+        if 3 not in idx[t]:
+            idx[t, 0] = 3
+    d = L().desc_from_shape(shape)
+    assert L().moe_stage_kernel(d, "gate_up") == "k_gateup_stream"
+    assert L().moe_stage_kernel(d, "down") == "k_down_stream"
+    y = _gpu_experts(d, dev, idx, w)
+    ref = oracle.experts(nb(dev["x"]), idx, w, *oracle_weights(dev))
+    got = to_f64(y)
+    assert rel_l2(got, ref) <= 5e-3
+    assert row_rel(got, ref).max() <= 1e-2
+
+
 def test_experts_full_size_sampled_rows():
     """Full-size shapes (H 2048, I 512), uneven buckets including one expert
     with many rows: every row of a sample of tokens against the oracle."""
