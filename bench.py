@@ -17,7 +17,8 @@ this host (`cpu_baseline`).
 The default workload (512 tokens: the weight-streaming, HBM-bound regime) is
 the headline; the same run measures the 16384-token layer with an expert bias
 (`large_batch`) and the 65536-token layer with skewed routing (`skew`), the
-MFMA regime, each with its own roofline, target and CPU baseline.
+MFMA regime, and the 256-token fp32 layer (`fp32`), each with its own
+roofline, target and CPU baseline.
 """
 import argparse
 import json
@@ -657,9 +658,10 @@ def bench_layer(L, shape, K, W, eager=False, balance=True, backward=True, cpu=Tr
 
 # The default run: the 512-token layer (HBM-bound weight stream) is the
 # headline; the 16384-token layer with bias and the 65536-token skewed layer
-# (the MFMA regime) are measured in the same run, each with its own roofline
-# and CPU baseline.
-EXTRA_WORKLOADS = (("large_batch", "full_t16k_bias"), ("skew", "skew_t64k"))
+# (the MFMA regime) and the small fp32 layer are measured in the same run,
+# each with its own roofline and CPU baseline (all cores, plus one thread for
+# the fp32 layer).
+EXTRA_WORKLOADS = (("large_batch", "full_t16k_bias"), ("skew", "skew_t64k"), ("fp32", "tiny_f32"))
 
 
 def main():
@@ -669,14 +671,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
                     help="one workload only (default: the 512-token headline plus the "
-                         "16384- and 65536-token layers)")
+                         "16384- and 65536-token layers and the fp32 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time steps launched one by one instead of a HIP graph of K steps")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
     ap.add_argument("--no-extra-workloads", action="store_true",
-                    help="with the default workload: skip the 16384- and 65536-token layers")
+                    help="with the default workload: skip the 16384- and 65536-token and fp32 layers")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the streaming-read and MFMA rates of this GPU")
     ap.add_argument("--backward-only", action="store_true",
