@@ -419,7 +419,7 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-template <int EPL>
+template <int EPL, int KSM>
 __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, int KS,
                                                  float* __restrict__ logits_out,
                                                  const float* __restrict__ bias,
@@ -433,15 +433,15 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, 
   float z[EPL], s[EPL], sb[EPL];
   bool valid[EPL];
   int bad = 0;
-  // issue every partial-sum load first (straight-line: a split past KS
-  // re-reads split 0, an element past E re-reads element E - 1; both are
-  // masked below), then add them in split order.  When every lane's EPL
-  // elements exist (E a multiple of 64 EPL: a wave-uniform test) they are
-  // read as 16-byte pieces.
-  float pv[kMaxKSplit][EPL];
+  // issue every partial-sum load first (straight-line over KSM >= KS splits,
+  // KSM fixed at compile time: a split past KS re-reads split 0, an element
+  // past E re-reads element E - 1; both are masked below), then add them in
+  // split order.  When every lane's EPL elements exist (E a multiple of
+  // 64 EPL: a wave-uniform test) they are read as 16-byte pieces.
+  float pv[KSM][EPL];
   if (EPL % 4 == 0 && E % (64 * EPL) == 0) {
 #pragma unroll
-    for (int k = 0; k < kMaxKSplit; ++k) {
+    for (int k = 0; k < KSM; ++k) {
       const float* row = part + ((size_t)(k < KS ? k : 0) * T + t) * E + lane * EPL;
 #pragma unroll
       for (int i = 0; i < EPL; i += 4) {
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, 
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kMaxKSplit; ++k) {
+    for (int k = 0; k < KSM; ++k) {
       const float* row = part + ((size_t)(k < KS ? k : 0) * T + t) * E;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) pv[k][i] = row[min(lane * EPL + i, E - 1)];
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, 
     valid[i] = lane * EPL + i < E;
     float acc = pv[0][i];
 #pragma unroll
-    for (int k = 1; k < kMaxKSplit; ++k)
+    for (int k = 1; k < KSM; ++k)
       if (k < KS) acc = acc + pv[k][i];
     z[i] = valid[i] ? acc : 0.0f;
   }
@@ -562,29 +562,53 @@ int select_epl(int E) {
   return epl;
 }
 
+template <int EPL>
+static void launch_select_epl(dim3 grid, hipStream_t s, const float* part, int ks,
+                              float* logits_out, const float* bias, int32_t* idx, float* w,
+                              uint32_t* status, int T, int E, int n_group, int topk_group, int K,
+                              float scale, int rec) {
+  // the K split is a power of two up to kMaxKSplit (logits_ksplit)
+  if (ks <= 1)
+    hipLaunchKernelGGL((k_select<EPL, 1>), grid, dim3(256), 0, s, part, ks, logits_out, bias, idx,
+                       w, status, T, E, n_group, topk_group, K, scale, rec);
+  else if (ks <= 2)
+    hipLaunchKernelGGL((k_select<EPL, 2>), grid, dim3(256), 0, s, part, ks, logits_out, bias, idx,
+                       w, status, T, E, n_group, topk_group, K, scale, rec);
+  else if (ks <= 4)
+    hipLaunchKernelGGL((k_select<EPL, 4>), grid, dim3(256), 0, s, part, ks, logits_out, bias, idx,
+                       w, status, T, E, n_group, topk_group, K, scale, rec);
+  else if (ks <= 8)
+    hipLaunchKernelGGL((k_select<EPL, 8>), grid, dim3(256), 0, s, part, ks, logits_out, bias, idx,
+                       w, status, T, E, n_group, topk_group, K, scale, rec);
+  else
+    hipLaunchKernelGGL((k_select<EPL, kMaxKSplit>), grid, dim3(256), 0, s, part, ks, logits_out,
+                       bias, idx, w, status, T, E, n_group, topk_group, K, scale, rec);
+}
+
 hipError_t launch_select(const float* part, int ks, float* logits_out, const float* bias,
                          int32_t* idx, float* w, uint32_t* status, int T, int E, int n_group,
                          int topk_group, int K, float scale, bool record_nonfinite, hipStream_t s,
                          const StageTimer* tm) {
+  if (ks < 1 || ks > kMaxKSplit) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((T + 3) / 4));
   const int rec = record_nonfinite ? 1 : 0;
   stage_begin(tm, kSelect, s);
   switch (select_epl(E)) {
     case 1:
-      hipLaunchKernelGGL(k_select<1>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
-                         status, T, E, n_group, topk_group, K, scale, rec);
+      launch_select_epl<1>(grid, s, part, ks, logits_out, bias, idx, w, status, T, E, n_group,
+                           topk_group, K, scale, rec);
       break;
     case 2:
-      hipLaunchKernelGGL(k_select<2>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
-                         status, T, E, n_group, topk_group, K, scale, rec);
+      launch_select_epl<2>(grid, s, part, ks, logits_out, bias, idx, w, status, T, E, n_group,
+                           topk_group, K, scale, rec);
       break;
     case 4:
-      hipLaunchKernelGGL(k_select<4>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
-                         status, T, E, n_group, topk_group, K, scale, rec);
+      launch_select_epl<4>(grid, s, part, ks, logits_out, bias, idx, w, status, T, E, n_group,
+                           topk_group, K, scale, rec);
       break;
     default:
-      hipLaunchKernelGGL(k_select<8>, grid, dim3(256), 0, s, part, ks, logits_out, bias, idx, w,
-                         status, T, E, n_group, topk_group, K, scale, rec);
+      launch_select_epl<8>(grid, s, part, ks, logits_out, bias, idx, w, status, T, E, n_group,
+                           topk_group, K, scale, rec);
       break;
   }
   stage_end(tm, kSelect, s);
