@@ -15,11 +15,15 @@
 //            weight rows 0..63 are gate rows, 64..127 up rows (K = H
 //            contiguous), token rows are the gathered x rows; h = silu(g) u
 //            is formed in registers.
-//   down (MODE 1): 128 output columns a slice (32 per wave); W_down[e] is
-//            [I][H], so the 128 weight rows are 128 consecutive k of the
-//            slice's columns, and the LDS transpose read turns them into the
-//            MFMA operand (4 consecutive k of one column per lane); token rows
-//            are the tile's h rows (contiguous, no gather).  K = I.
+//   down (MODE 1): 256 output columns a slice (64 per wave), stages 64
+//            deep: W_down[e] is [I][H], so a stage holds 64 consecutive k
+//            rows of the slice's columns (512 bytes each), and the LDS
+//            transpose read turns them into the MFMA operand (4 consecutive k
+//            of one column per lane); the token rows are the tile's h rows
+//            (contiguous, no gather), 128 bytes each, so they are 1/8 of a
+//            stage's 36 KiB.  K = I.  (A layout of 128 columns and 128-deep
+//            stages, h rows 1/4 of the bytes and items of half as many
+//            stages, ran at 106 us against 98 at 512 tokens.)
 // Four stage buffers (160 KiB, all of the CU's LDS) form a ring filled by
 // direct global -> LDS loads (global_load_lds_dwordx4: each wave instruction
 // writes 1 KiB, lane l at +16 l), three stages in flight while one is
@@ -40,7 +44,8 @@ constexpr int kStageB = 40960;  // bytes per stage
 constexpr int kSBK = 128;       // K depth of a stage
 constexpr int kSRowB = 256;     // bytes per staged row
 constexpr int kSFeat = 64;      // gate/up features per item
-constexpr int kSOut = 128;      // down output columns per item
+constexpr int kSOut = 256;      // bf16 down output columns per item
+constexpr int kSOutF32 = 128;   // fp32 down output columns per item
 
 // One stage's loads of this wave: load g (0..9) brings the lane's 16 bytes
 // from base[g] + off[g] (a wave-uniform 64-bit base plus a 32-bit per-lane
@@ -80,6 +85,31 @@ __device__ __forceinline__ void dma_stage(const void* const (&base)[10], const u
       : "memory", "scc");
 }
 
+// The first nine of dma_stage's loads (a stage of 64 rows of 512 bytes and
+// 32 rows of 128 bytes: 36 KiB).
+__device__ __forceinline__ void dma_stage9(const void* const (&base)[10], const uint32_t (&off)[10],
+                                           uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %19\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %10 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %11 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %12 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %13 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %14 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, %15 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %7, %16 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %8, %17 nt\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, %18\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]),
+        "v"(off[7]), "v"(off[8]), "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3]),
+        "s"(base[4]), "s"(base[5]), "s"(base[6]), "s"(base[7]), "s"(base[8]), "s"(lds)
+      : "memory", "scc");
+}
+
 struct GItem {
   int e, row0, nrows, i0;  // expert (E = shared), first row, rows, first feature / column
 };
@@ -114,10 +144,13 @@ __device__ __forceinline__ int f32d_chunk(int r, int c) { return c ^ (((r >> 2) 
 //   MODE 0 (gate/up, bf16): weight row r < 64 is gate row i0 + r, r >= 64 up
 //     row i0 + r - 64, K columns 128 s .. of stage s (256 bytes); chunk c at
 //     sswz(r, c).
-//   MODE 1 (down, bf16): weight row r is W_down row (k) 128 s + r at columns
-//     i0 .. i0 + 127; chunk c at r * 256 + 16 (c ^ wd_swz(r)), the layout the
-//     transpose read wants (16 rows read at one 32-byte window meet two to a
-//     window).
+//   MODE 1 (down, bf16): weight row r (of 64) is W_down row 64 s + r at
+//     columns i0 .. i0 + 255 (512 bytes), chunk c at r * 512 + 16
+//     (c ^ wd_swz(r)) (the layout of k_expert_gemm's down slices: the
+//     transpose reads of 16 rows at one 32-byte window meet two to a
+//     window); the 32 token rows (128 bytes, K columns 64 s ..) follow at
+//     32 KiB, chunk c of row n at rs_addr(n, c); one token load a wave
+//     (9 loads a stage).
 //   MODE 2 (gate/up, fp32): as MODE 0 with fp32 rows: K columns 64 s .. (256
 //     bytes), 64 features an item.
 //   MODE 3 (down, fp32): weight row r (of 64) is W_down row 64 s + r at
@@ -125,14 +158,16 @@ __device__ __forceinline__ int f32d_chunk(int r, int c) { return c ^ (((r >> 2) 
 //     f32d_chunk(r, c); token rows carry K columns 64 s ...
 template <int MODE>
 __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
-  constexpr bool kDown = (MODE & 1) != 0;
-  constexpr bool kF32 = MODE >= 2;
+  constexpr bool kDown = MODE == 1 || MODE == 3;
+  constexpr bool kF32 = MODE == 2 || MODE == 3;
+  constexpr bool kWide = MODE == 1;  // bf16 down: 512-byte weight rows, 128-byte token rows
   typedef typename std::conditional<kF32, float, uint16_t>::type elt_t;
   constexpr int kEl = sizeof(elt_t);
-  constexpr int kSK = kF32 ? 64 : kSBK;  // K depth of a stage
-  constexpr int kCols = kDown ? kSOut : kSFeat;  // output columns (features) an item
-  constexpr int kLoads = 10;  // loads per wave per stage
-  constexpr int kStores = MODE == 3 ? 4 : 2;  // epilogue stores per wave
+  constexpr int kSK = (kF32 || kWide) ? 64 : kSBK;  // K depth of a stage
+  constexpr int kCols = MODE == 1 ? kSOut : MODE == 3 ? kSOutF32 : kSFeat;  // output columns an item
+  constexpr int kLoads = kWide ? 9 : 10;  // loads per wave per stage
+  constexpr int kStores = (MODE == 3 || kWide) ? 4 : 2;  // epilogue stores per wave
+  constexpr int kAT = kWide ? 4 : 2;  // accumulator tiles a token tile
   // with at least 4 stages an item the epilogue's item is one of the last two
   // the issue cursor started (fp32 down items may have fewer: re-read)
   constexpr bool kKeepItems = MODE != 3;
@@ -196,10 +231,12 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
     if (MODE == 3) {
       const int r = 8 * j + 2 * w + (lane >> 5);
       off[j] = (uint32_t)(r * H * 4 + (f32d_chunk(r, lane & 31) << 4));
+    } else if (kWide) {
+      const int r = 8 * j + 2 * w + (lane >> 5);
+      off[j] = (uint32_t)(r * H * 2 + (((lane & 31) ^ wd_swz(r)) << 4));
     } else {
       const int r = 16 * j + 4 * w + (lane >> 4);
-      off[j] = kDown ? (uint32_t)(r * H * 2 + (((lane & 15) ^ wd_swz(r)) << 4))
-                     : (uint32_t)((r & 63) * H * kEl + (((lane & 15) ^ (r & 15)) << 4));
+      off[j] = (uint32_t)((r & 63) * H * kEl + (((lane & 15) ^ (r & 15)) << 4));
     }
   }
   int32_t ptok[2];  // gate/up: sorted pairs of the token rows of the next item (gathered)
@@ -254,11 +291,18 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
         ub = gb;
         tb = reinterpret_cast<const uint8_t*>(
             uniform_ptr(hr_p + (sh ? sh_h : 0) + (size_t)it.row0 * I));
+        if (kWide) {
+          // one load: token rows 8 w + lane / 8, 128 bytes (64 k) each
+          const int r = 8 * w + (lane >> 3);
+          const int tr = min(r, it.nrows - 1);
+          off[8] = (uint32_t)(tr * I * 2 + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
+        } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = 16 * (8 + j) + 4 * w + (lane >> 4);
-          const int tr = min(r - 128, it.nrows - 1);
-          off[8 + j] = (uint32_t)(tr * I * kEl + (((lane & 15) ^ (r & 15)) << 4));
+          for (int j = 0; j < 2; ++j) {
+            const int r = 16 * (8 + j) + 4 * w + (lane >> 4);
+            const int tr = min(r - 128, it.nrows - 1);
+            off[8 + j] = (uint32_t)(tr * I * kEl + (((lane & 15) ^ (r & 15)) << 4));
+          }
         }
       }
     }
@@ -267,51 +311,64 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
     // stage advance: gate/up weights and all token rows move 256 bytes along
     // K; down weights move kSK rows
     const size_t kw = kDown ? (size_t)sk * kSK * H * kEl : (size_t)sk * kSRowB;
-    const int kt = sk * kSRowB;
+    const int kt = sk * kSK * kEl;
     const void* bk[10];
 #pragma unroll
     for (int j = 0; j < 10; ++j)
       bk[j] = reinterpret_cast<const uint8_t*>(base[j]) + (j < 8 ? kw : (size_t)kt);
-    dma_stage(bk, off, lds);
+    if (kWide) dma_stage9(bk, off, lds);
+    else dma_stage(bk, off, lds);
     if (++sk == nst) sk = 0;
   };
 
   // acc[t][n]: gate/up: t = 0 gate, 1 up, features 16 w + (MFMA row) of
   // token tile n; down: column tile t (see below), token tile n
-  f32x4 acc[2][2];
+  f32x4 acc[kAT][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < kAT; ++t)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // MODE 1 transpose reads: lane 4 c + m of group q points at k row
-  // 32 u + 8 q + c (+ 4 for the second read) and columns 32 w + 8 m + 4 t ..
-  // + 3 of the item's 128 (chunk 4 w + m, half t), so column tile t's MFMA
-  // row 4 q' + i is column 32 w + 8 q' + 4 t + i: tiles 0 and 1 give each
-  // lane 8 consecutive columns (one 16-byte store).  Rows 8 q + c and + 4
-  // share their swizzle.
-  const int dn_lane =
-      (8 * q + (r16 >> 2)) * kSRowB + (((4 * w + (r16 & 3)) ^ wd_swz(8 * q + (r16 >> 2))) << 4);
   // fp32 (16x16x4 MFMA, one element of A and of B a lane): K block b of 16
   // is read as 16-byte chunks 4 b + q (k = 16 b + 4 q .. + 3) and MFMA j of
   // the block takes element j, i.e. k = 16 b + 4 q + j from lane group q.
   // MODE 3's A operand (W_down[k][column]) is read element by element: lane
   // (m, q) takes k row 16 b + 4 q + j at column 32 w + 16 t + m.
+  // MODE 1 transpose reads: lane 4 c + m of group q points at k row
+  // 32 u + 8 q + c (+ 4 for the second read, which shares the row's swizzle)
+  // and columns 64 w + 32 (t / 2) + 8 m + 4 (t % 2) .. + 3 (chunk
+  // 8 w + 4 (t / 2) + m, half t % 2), so column tile t's MFMA row 4 q' + i is
+  // column 64 w + 32 (t / 2) + 8 q' + 4 (t % 2) + i and tiles 2 v, 2 v + 1
+  // give each lane the 8 columns 64 w + 32 v + 8 q' .. + 7.
+  const int wd_row = 8 * q + (r16 >> 2);
+  const int wd_lane = wd_row * 512 + ((((8 * w + (r16 & 3)) ^ wd_swz(wd_row))) << 4);
   auto compute = [&](int c) __attribute__((always_inline)) {
     const uint8_t* st = ring + (c & 3) * kStageB;
-    if (!kF32) {
+    if (kWide) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 A[4], B[2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // chunk 8 w + 4 (t / 2) + m: the XOR with wd_swz (even, < 16) keeps
+          // bit 2 of the chunk, so 4 (t / 2) moves the swizzled chunk by 4
+          const uint8_t* p =
+              st + 32 * u * 512 + (wd_lane ^ ((4 * (t >> 1)) << 4)) + 8 * (t & 1);
+          const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * 512);
+          A[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) B[n] = lds16(st + 32768 + rs_addr(16 * n + r16, 4 * u + q));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[t][n] = mfma16x16x32(A[t], B[n], acc[t][n]);
+      }
+    } else if (!kF32) {
       u32x4 A0[4], A1[4], B[4][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (!kDown) {
-          A0[u] = lds16(st + sswz(16 * w + r16, 4 * u + q));
-          A1[u] = lds16(st + sswz(64 + 16 * w + r16, 4 * u + q));
-        } else {
-          const uint8_t* p = st + 32 * u * kSRowB + dn_lane;
-          u32x2 l0 = lds_tr16(p), h0 = lds_tr16(p + 4 * kSRowB);
-          u32x2 l1 = lds_tr16(p + 8), h1 = lds_tr16(p + 8 + 4 * kSRowB);
-          A0[u] = u32x4{l0.x, l0.y, h0.x, h0.y};
-          A1[u] = u32x4{l1.x, l1.y, h1.x, h1.y};
-        }
+        A0[u] = lds16(st + sswz(16 * w + r16, 4 * u + q));
+        A1[u] = lds16(st + sswz(64 + 16 * w + r16, 4 * u + q));
 #pragma unroll
         for (int n = 0; n < 2; ++n) B[u][n] = lds16(st + sswz(128 + 16 * n + r16, 4 * u + q));
       }
@@ -360,9 +417,10 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   };
   // epilogue: exactly kStores stores per wave (rows past the tile end go to
   // trash).  MODE 0: lane holds features i0 + 16 w + 4 q + 0..3 of token row
-  // 16 n + r16 (bf16, 8 bytes); MODE 1: columns i0 + 32 w + 8 q + 0..7 (16
-  // bytes); MODE 2: features i0 + 16 w + 4 q + 0..3 (fp32, 16 bytes); MODE 3:
-  // columns i0 + 32 w + 16 t + 4 q + 0..3 of column tile t (fp32, 16 bytes).
+  // 16 n + r16 (bf16, 8 bytes); MODE 1: columns i0 + 64 w + 32 v + 8 q + 0..7
+  // for v = 0, 1 (two 16-byte stores); MODE 2: features i0 + 16 w + 4 q +
+  // 0..3 (fp32, 16 bytes); MODE 3: columns i0 + 32 w + 16 t + 4 q + 0..3 of
+  // column tile t (fp32, 16 bytes).
   auto epilogue = [&](const GItem& it) __attribute__((always_inline)) {
     const bool sh = it.e >= E;
 #pragma unroll
@@ -384,14 +442,17 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
                             __float_as_uint(hv[2]), __float_as_uint(hv[3])};
           store16(reinterpret_cast<uint16_t*>(ok ? hb + (size_t)row * I : trash), pk);
         }
-      } else if (MODE == 1) {
-        elt_t* ob = or_p + (sh ? sh_o : 0) + (size_t)it.row0 * H + it.i0 + 32 * w + 8 * q;
-        u32x4 pk;
-        pk.x = pack_bf16x2(acc[0][n][0], acc[0][n][1]);
-        pk.y = pack_bf16x2(acc[0][n][2], acc[0][n][3]);
-        pk.z = pack_bf16x2(acc[1][n][0], acc[1][n][1]);
-        pk.w = pack_bf16x2(acc[1][n][2], acc[1][n][3]);
-        store16(reinterpret_cast<uint16_t*>(ok ? ob + (size_t)row * H : trash), pk);
+      } else if (kWide) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          elt_t* ob = or_p + (sh ? sh_o : 0) + (size_t)it.row0 * H + it.i0 + 64 * w + 32 * v + 8 * q;
+          u32x4 pk;
+          pk.x = pack_bf16x2(acc[2 * v][n][0], acc[2 * v][n][1]);
+          pk.y = pack_bf16x2(acc[2 * v][n][2], acc[2 * v][n][3]);
+          pk.z = pack_bf16x2(acc[2 * v + 1][n][0], acc[2 * v + 1][n][1]);
+          pk.w = pack_bf16x2(acc[2 * v + 1][n][2], acc[2 * v + 1][n][3]);
+          store16(reinterpret_cast<uint16_t*>(ok ? ob + (size_t)row * H : trash), pk);
+        }
       } else {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -402,7 +463,7 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
         }
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < kAT; ++t) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
@@ -457,9 +518,10 @@ bool stream_ring_ok(const ExpertArgs& a) {
 }
 
 bool down_stream_ok(const ExpertArgs& a) {
-  // whole stages and column slices; weight lane offsets (128 rows) 32-bit
-  return stream_ring_ok(a) && a.I % kSBK == 0 && a.I / kSBK >= 4 && a.H % kSOut == 0 &&
-         (int64_t)kSBK * a.H * 2 < (int64_t(1) << 31);
+  // 256-column items of whole 64-deep stages, at least 4 an item; weight lane
+  // offsets (64 rows) 32-bit
+  return stream_ring_ok(a) && a.H % kSOut == 0 && a.I % 64 == 0 && a.I / 64 >= 4 &&
+         (int64_t)64 * a.H * 2 < (int64_t(1) << 31);
 }
 
 static dim3 stream_grid(int64_t items) {
@@ -490,7 +552,7 @@ bool stream_f32_ok(const ExpertArgs& a) {
 
 hipError_t launch_stream_f32(const ExpertArgs& a, int64_t tiles, hipStream_t s,
                              const StageTimer* tm) {
-  const int gslices = a.I / kSFeat, dslices = a.H / kSOut;
+  const int gslices = a.I / kSFeat, dslices = a.H / kSOutF32;
   stage_begin(tm, kGateUp, s);
   hipLaunchKernelGGL(k_gateup_stream_f32, stream_grid(tiles * gslices), dim3(256), 0, s, a,
                      gslices);
@@ -503,8 +565,8 @@ hipError_t launch_stream_f32(const ExpertArgs& a, int64_t tiles, hipStream_t s,
 
 hipError_t launch_down_stream_bf16(const ExpertArgs& a, int64_t tiles, hipStream_t s,
                                    const StageTimer* tm) {
-  const int slices = a.H / kSOut;
   stage_begin(tm, kDown, s);
+  const int slices = a.H / kSOut;
   hipLaunchKernelGGL(k_down_stream, stream_grid(tiles * slices), dim3(256), 0, s, a, slices);
   stage_end(tm, kDown, s);
   return hipGetLastError();

@@ -399,11 +399,14 @@ def test_experts_f32_stream_shapes(T, H, I, Is, hot):
 
 
 @pytest.mark.parametrize("T,H,I,Is,hot", [(200, 1024, 640, 640, 0), (64, 512, 1024, 0, 0),
-                                           (300, 2048, 512, 0, 120)])
+                                           (300, 2048, 512, 0, 120), (150, 768, 256, 256, 60),
+                                           (90, 1280, 192, 192, 0)])
 def test_experts_bf16_stream_shapes(T, H, I, Is, hot):
-    """bf16 weight-streaming path at other widths: 5- and 8-stage down items
-    (I = 640, 1024), 4 and 8 down column slices (H = 512, 1024), no shared
-    expert, and a hot expert with several tiles."""
+    """bf16 weight-streaming path at other widths: down items of 4 to 16
+    stages (I = 256 .. 1024), 2 to 8 down column slices of 256 (H = 512 ..
+    2048, 1280), no shared expert, a hot expert with several tiles, and
+    I = 192 (the register-streaming down kernel next to the gate/up
+    stream)."""
     say("experts bf16 stream", T, H, I, Is, hot)
     shape = synth.small_shape(T, H=H, I=I, I_shared=Is, dtype="bf16", seed=740 + T)
     dev = make_layer(shape)
@@ -414,7 +417,7 @@ def test_experts_bf16_stream_shapes(T, H, I, Is, hot):
             idx[t, 0] = 3
     d = L().desc_from_shape(shape)
     assert L().moe_stage_kernel(d, "gate_up") == "k_gateup_stream"
-    assert L().moe_stage_kernel(d, "down") == "k_down_stream"
+    assert L().moe_stage_kernel(d, "down") == ("k_down_stream" if I >= 256 else "k_down_bf16")
     y = _gpu_experts(d, dev, idx, w)
     ref = oracle.experts(nb(dev["x"]), idx, w, *oracle_weights(dev))
     got = to_f64(y)
