@@ -265,6 +265,11 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   // items started (the epilogue's, kept so that it reads no table entry)
   int sm = -1, sk = 0;
   GItem prev{}, cur{};
+  // rows of the item of the stage in ring slot b, byte b (a tile holds at
+  // most 32 rows): compute skips the second 16-row token tile when the item
+  // has at most 16 rows (its accumulators stay zero; the epilogue sends those
+  // rows to trash)
+  uint32_t ring_rows = 0;
   const uint8_t *gb = nullptr, *ub = nullptr, *tb = nullptr;
   auto issue = [&](int c) __attribute__((always_inline)) {
     if (sk == 0) {
@@ -308,6 +313,7 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
     }
     const void* base[10] = {gb, gb, gb, gb, ub, ub, ub, ub, tb, tb};
     const uint32_t lds = ring0_of(ring, c & 3, w);
+    ring_rows = (ring_rows & ~(0xffu << (8 * (c & 3)))) | ((uint32_t)cur.nrows << (8 * (c & 3)));
     // stage advance: gate/up weights and all token rows move 256 bytes along
     // K; down weights move kSK rows
     const size_t kw = kDown ? (size_t)sk * kSK * H * kEl : (size_t)sk * kSRowB;
@@ -341,12 +347,13 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
   // give each lane the 8 columns 64 w + 32 v + 8 q' .. + 7.
   const int wd_row = 8 * q + (r16 >> 2);
   const int wd_lane = wd_row * 512 + ((((8 * w + (r16 & 3)) ^ wd_swz(wd_row))) << 4);
-  auto compute = [&](int c) __attribute__((always_inline)) {
+  auto compute_nt = [&](int c, auto ntc) __attribute__((always_inline)) {
+    constexpr int NT = decltype(ntc)::value;  // 16-row token tiles computed
     const uint8_t* st = ring + (c & 3) * kStageB;
     if (kWide) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        u32x4 A[4], B[2];
+        u32x4 A[4], B[2] = {};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           // chunk 8 w + 4 (t / 2) + m: the XOR with wd_swz (even, < 16) keeps
@@ -357,35 +364,35 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
           A[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
 #pragma unroll
-        for (int n = 0; n < 2; ++n) B[n] = lds16(st + 32768 + rs_addr(16 * n + r16, 4 * u + q));
+        for (int n = 0; n < NT; ++n) B[n] = lds16(st + 32768 + rs_addr(16 * n + r16, 4 * u + q));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int n = 0; n < 2; ++n) acc[t][n] = mfma16x16x32(A[t], B[n], acc[t][n]);
+          for (int n = 0; n < NT; ++n) acc[t][n] = mfma16x16x32(A[t], B[n], acc[t][n]);
       }
     } else if (!kF32) {
-      u32x4 A0[4], A1[4], B[4][2];
+      u32x4 A0[4], A1[4], B[4][2] = {};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         A0[u] = lds16(st + sswz(16 * w + r16, 4 * u + q));
         A1[u] = lds16(st + sswz(64 + 16 * w + r16, 4 * u + q));
 #pragma unroll
-        for (int n = 0; n < 2; ++n) B[u][n] = lds16(st + sswz(128 + 16 * n + r16, 4 * u + q));
+        for (int n = 0; n < NT; ++n) B[u][n] = lds16(st + sswz(128 + 16 * n + r16, 4 * u + q));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
+        for (int n = 0; n < NT; ++n) {
           acc[0][n] = mfma16x16x32(A0[u], B[u][n], acc[0][n]);
           acc[1][n] = mfma16x16x32(A1[u], B[u][n], acc[1][n]);
         }
     } else {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        f32x4 B[2];
+        f32x4 B[2] = {};
         float A[2][4];  // [t][j]: the A element of MFMA j of operand t
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
           B[n] = __builtin_bit_cast(f32x4, lds16(st + sswz(128 + 16 * n + r16, 4 * b + q)));
         if (!kDown) {
 #pragma unroll
@@ -408,13 +415,19 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int n = 0; n < 2; ++n)
+          for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
               acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[t][j], B[n][j], acc[t][n], 0, 0, 0);
       }
     }
+  };  auto compute = [&](int c) __attribute__((always_inline)) {
+    if (((ring_rows >> (8 * (c & 3))) & 0xffu) > 16u)
+      compute_nt(c, std::integral_constant<int, 2>());
+    else
+      compute_nt(c, std::integral_constant<int, 1>());
   };
+
   // epilogue: exactly kStores stores per wave (rows past the tile end go to
   // trash).  MODE 0: lane holds features i0 + 16 w + 4 q + 0..3 of token row
   // 16 n + r16 (bf16, 8 bytes); MODE 1: columns i0 + 64 w + 32 v + 8 q + 0..7
