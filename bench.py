@@ -664,6 +664,88 @@ def bench_layer(L, shape, K, W, eager=False, balance=True, backward=True, cpu=Tr
 EXTRA_WORKLOADS = (("large_batch", "full_t16k_bias"), ("skew", "skew_t64k"), ("fp32", "tiny_f32"))
 
 
+def library_gemm(L, synth, reps=20):
+    """Context for the 16384-token layer's MFMA fraction: what the platform's
+    BLAS (torch bf16 matmul / bmm, i.e. hipBLASLt) reaches on this GPU on a
+    dense 8192^3 product and on the per-expert products of a perfectly
+    balanced routing (256 experts x 512 rows, contiguous rows, operands in the
+    library's preferred layout, no gather, no SwiGLU, no combine), beside
+    libmoe's moe_permute + moe_experts on that same balanced routing (gathered
+    rows, SwiGLU, shared expert and combine included).  Event-timed mean of
+    `reps` calls after 3 untimed ones."""
+    import torch
+    dev = "cuda"
+
+    # operands drawn like the layer's own inputs (synth): token rows N(0, 1)
+    # from the CPU generator, weights N(0, 0.02) from the GPU generator (the
+    # MFMA rate under load depends on the operand bits: the clock is power
+    # limited, and zero operands run faster)
+    def tokens(*s):
+        return synth._normal(s, 1.0, 11, "cpu", torch.bfloat16).to(dev)
+
+    def weights(*s):
+        return synth._normal(s, 0.02, 12, dev, torch.bfloat16)
+
+    def mean_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def entry(flop, ms):
+        return {"us": round(ms * 1e3, 1), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(flop / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+
+    out = {"what": "bf16; library = torch.matmul / torch.bmm (hipBLASLt), "
+                   "libmoe = moe_permute + moe_experts through the C ABI"}
+    n = 8192
+    A, B = tokens(n, n), weights(n, n)
+    out["library_dense_8192"] = entry(2 * n ** 3, mean_ms(lambda: torch.matmul(A, B)))
+    del A, B
+    shape = synth.WORKLOADS["full_t16k_bias"]
+    T, H, E, K, I, Is = shape.T, shape.H, shape.E, shape.top_k, shape.I, shape.I_shared
+    M = T * K // E
+    xe, wgu = tokens(E, M, H), weights(E, H, 2 * I)  # gate and up side by side
+    flop_gu = 2 * E * M * H * 2 * I
+    out["library_bmm_gate_up"] = entry(flop_gu, mean_ms(lambda: torch.bmm(xe, wgu)))
+    xe.zero_()
+    wgu.zero_()
+    out["library_bmm_gate_up_zero_operands"] = entry(flop_gu, mean_ms(lambda: torch.bmm(xe, wgu)))
+    del xe, wgu
+    he, wd = tokens(E, M, I), weights(E, I, H)
+    out["library_bmm_down"] = entry(2 * E * M * I * H, mean_ms(lambda: torch.bmm(he, wd)))
+    del he, wd
+    # libmoe on the balanced routing: pair p = t K + j goes to expert p mod E
+    # (E divides T K: every expert gets T K / E rows, a token's K experts differ)
+    d = L.desc_from_shape(shape)
+    w = synth.expert_weights(shape, device=dev)
+    x = synth.router_inputs(shape)[0].to(dev)
+    idx = (torch.arange(T * K, dtype=torch.int32, device=dev) % E).view(T, K)
+    topk_w = torch.full((T, K), 1.0 / K, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * K, dtype=torch.int32, device=dev)
+    ps = torch.empty(T * K, dtype=torch.int32, device=dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ws = L.alloc_workspace(d, dev)
+
+    def ours():
+        L.moe_permute(d, idx, counts, offsets, sp, ps, None, ws)
+        L.moe_experts(d, x, topk_w, offsets, sp, ps, w, y, ws)
+
+    flop = 2 * 3 * H * (T * K * I + T * Is)
+    out["libmoe_experts_balanced"] = entry(flop, mean_ms(ours))
+    out["libmoe_experts_balanced"]["rows_per_expert"] = int(counts.min().item())
+    out["libmoe_experts_balanced"]["kernels"] = [L.moe_stage_kernel(d, s) for s in ("gate_up", "down")]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -691,6 +773,9 @@ def main():
                     help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this "
                          "workload and of --copy-calibration into profiles/traffic.json")
     ap.add_argument("--profile-note", default="", help="with --write-traffic: the summary file")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only compare torch's bf16 GEMMs (hipBLASLt) with libmoe's experts on a "
+                         "balanced 16384-token routing (prints its JSON object)")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(args.workload or "full_t512", *args.write_traffic,
@@ -715,8 +800,11 @@ def main():
     from group_limited_top_amd import _lib as L
     from group_limited_top_amd import synth
 
-    shape = synth.WORKLOADS[args.workload or "full_t512"]
     torch.cuda.set_device(0)
+    if args.library_gemm:
+        print(json.dumps({"library_gemm": library_gemm(L, synth)}), flush=True)
+        return
+    shape = synth.WORKLOADS[args.workload or "full_t512"]
     if shape.layers != 1:
         print(json.dumps(bench_stack(L, shape, min(args.steps, 10), min(args.warmup, 2))), flush=True)
         return
