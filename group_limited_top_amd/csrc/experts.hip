@@ -298,7 +298,8 @@ __global__ __launch_bounds__(256) void k_down_bf16(const ExpertArgs a, int hslic
 // KT > 0: top_k == KT known at compile time (fewer registers: more waves in
 // flight); KT == 0: any top_k <= 16.  A block takes NT consecutive tokens;
 // each thread one 16-byte chunk of all their rows, every row load issued
-// before any arithmetic.
+// before any arithmetic.  The rows are read once: nontemporal loads (138.7 ->
+// 112.6 us at 16384 tokens, 4.9 -> 6.0 TB/s).
 template <int KT, int NT>
 __global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
   constexpr int kMaxK = KT > 0 ? KT : 16;  // top_k <= 16 (the supported envelope)
@@ -325,10 +326,10 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const ExpertArgs a) {
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       const int t = min(t0 + u, T - 1);
-      vs[u] = a.Is > 0 ? ld16(osh + (size_t)t * H + c * 8) : zero4;
+      vs[u] = a.Is > 0 ? ld16_stream(osh + (size_t)t * H + c * 8) : zero4;
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j)
-        v[u][j] = slot[u][j] >= 0 ? ld16(orr + (size_t)slot[u][j] * H + c * 8) : zero4;
+        v[u][j] = slot[u][j] >= 0 ? ld16_stream(orr + (size_t)slot[u][j] * H + c * 8) : zero4;
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
@@ -673,11 +674,11 @@ __global__ __launch_bounds__(256) void k_combine_f32(const ExpertArgs a) {
   }
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
-    const f32x4 vs = a.Is > 0 ? *reinterpret_cast<const f32x4*>(osh + (size_t)t * H + 4 * c) : zero4;
+    const f32x4 vs = a.Is > 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(osh + (size_t)t * H + 4 * c)) : zero4;
     f32x4 v[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      v[j] = slot[j] >= 0 ? *reinterpret_cast<const f32x4*>(orr + (size_t)slot[j] * H + 4 * c) : zero4;
+      v[j] = slot[j] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(orr + (size_t)slot[j] * H + 4 * c)) : zero4;
     // j order, one product and one sum per term, as specified
     f32x4 acc = vs;
 #pragma unroll
