@@ -373,8 +373,10 @@ hipError_t launch_logits_f32(const float* x, const float* w, float* logits, int 
 //                         the others are masked to -inf; then top_k rounds of
 //                         a wave-wide maximum of 64-bit keys (orderable sb,
 //                         then the complement of the expert index, so that
-//                         ties go to the lower index), by DPP within 16-lane
-//                         rows and readlane across rows
+//                         ties go to the lower index): each lane's best key,
+//                         the 32-bit maximum of their score halves (DPP
+//                         within 16-lane rows, readlane across rows), and the
+//                         lowest lane holding it
 //   [Routing §二 step 3]  S = fp32 sum of the chosen unbiased scores in choice
 //                         order, w_j = RN(RN(s_j / RN(S + 1e-20)) * scale)
 // ----------------------------------------------------------------------------
@@ -383,36 +385,18 @@ __device__ __forceinline__ uint32_t orderable(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Maximum over the 64 lanes, returned in every lane.  All lanes must be active.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint64_t o = dpp_u64<0xB1>(v);  // quad_perm [1,0,3,2]
-  v = o > v ? o : v;
-  o = dpp_u64<0x4E>(v);  // quad_perm [2,3,0,1]
-  v = o > v ? o : v;
-  o = dpp_u64<0x141>(v);  // row_half_mirror
-  v = o > v ? o : v;
-  o = dpp_u64<0x140>(v);  // row_mirror: every lane holds its 16-lane row maximum
-  v = o > v ? o : v;
-  uint64_t m = readlane_u64(v, 0);
-  uint64_t m1 = readlane_u64(v, 16);
-  m = m1 > m ? m1 : m;
-  m1 = readlane_u64(v, 32);
-  m = m1 > m ? m1 : m;
-  m1 = readlane_u64(v, 48);
-  return m1 > m ? m1 : m;
+// Wave-wide maximum of a 32-bit unsigned value (DPP within 16-lane rows,
+// readlane across rows), returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, true));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, true));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, true));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, true));  // row_mirror
+  const uint32_t m01 = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t m23 = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(m01, m23);
 }
 
 __device__ __forceinline__ float readlane_f32(float v, int l) {
@@ -532,9 +516,16 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ part, 
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
-    const uint64_t m = wave_max_u64(best);
-    const int e = (int)(0xffffffffu - (uint32_t)m);
-    const int owner = e / EPL, slot = e % EPL;
+    // the wave's largest key: its score half by a 32-bit maximum, then the
+    // lowest lane holding that score (lane l holds experts l EPL .. l EPL +
+    // EPL - 1, and a lane's best already prefers its lower index on a tie),
+    // which is the 64-bit maximum of (score, complemented index)
+    const uint32_t hi = (uint32_t)(best >> 32);
+    const uint32_t mhi = wave_max_u32(hi);
+    const int owner = (int)__builtin_ctzll(__ballot(hi == mhi));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, owner);
+    const int e = (int)(0xffffffffu - lo);
+    const int slot = e % EPL;
     float sv = s[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i)
