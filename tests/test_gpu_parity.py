@@ -309,6 +309,38 @@ def test_permute_bit_exact(T, kind):
     assert Lb.moe_status(ws) == 0
 
 
+@pytest.mark.parametrize("T,E,n_group,kind", [(65536, 256, 8, "skew"), (20000, 192, 6, "uniform"),
+                                              (40000, 512, 8, "uniform"),
+                                              (2100, 384, 6, "uniform")])
+def test_permute_bit_exact_chunked(T, E, n_group, kind):
+    """The chunked path (more than 16384 pairs) at up to 256 chunks of up to
+    2048 pairs, and expert counts that are not a power of two (the chunk scan
+    splits each expert's chunks over 1024 / E-rounded-up threads)."""
+    say("permute chunked", T, E, kind)
+    Lb = L()
+    rng = np.random.default_rng(T + E)
+    K = 8
+    if kind == "uniform":
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    else:
+        idx = (rng.zipf(1.3, (T, K)).astype(np.int64) % E).astype(np.int32)
+    d = Lb.make_desc(T, 2048, E=E, n_group=n_group)
+    it = torch.from_numpy(idx).to(DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    sp = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    ps = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    ws = Lb.alloc_workspace(d, DEV)
+    Lb.moe_permute(d, it, counts, offsets, sp, ps, None, ws)
+    torch.cuda.synchronize()
+    c, o, s, p = oracle.permute(idx, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o)
+    np.testing.assert_array_equal(sp.cpu().numpy(), s)
+    np.testing.assert_array_equal(ps.cpu().numpy(), p)
+    assert Lb.moe_status(ws) == 0
+
+
 # --------------------------------------------------------------------------- experts
 
 def _random_routing(rng, T, E, K):
