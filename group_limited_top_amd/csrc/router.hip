@@ -15,6 +15,26 @@ namespace moe {
 // the final conversion rounds to nearest even, so the value is reproducible
 // bit for bit by any IEEE implementation of the same steps.
 // ----------------------------------------------------------------------------
+// The Taylor coefficients RN(1/i!), i = 13 .. 2, of exp on the reduced
+// argument.  They are read from memory (scalar loads into SGPRs) rather than
+// written as literals: each Horner step is then one fma with an SGPR-pair
+// operand, where a literal would first be moved into VGPRs for every
+// evaluation.  Nothing writes this table.
+__device__ double kExpTaylor[12] = {
+    0x1.6124613a86d09p-33,  // 1/13!
+    0x1.1eed8eff8d898p-29,  // 1/12!
+    0x1.ae64567f544e4p-26,  // 1/11!
+    0x1.27e4fb7789f5cp-22,  // 1/10!
+    0x1.71de3a556c734p-19,  // 1/9!
+    0x1.a01a01a01a01ap-16,  // 1/8!
+    0x1.a01a01a01a01ap-13,  // 1/7!
+    0x1.6c16c16c16c17p-10,  // 1/6!
+    0x1.1111111111111p-7,   // 1/5!
+    0x1.5555555555555p-5,   // 1/4!
+    0x1.5555555555555p-3,   // 1/3!
+    0x1.0p-1,               // 1/2!
+};
+
 __device__ __forceinline__ float sigmoid32(float z) {
   if (!(z == z)) return z;
   const double t = -(double)z;
@@ -25,18 +45,9 @@ __device__ __forceinline__ float sigmoid32(float z) {
   double r = __builtin_fma(-n, 0x1.62e42fefa39efp-1, t);
   r = __builtin_fma(-n, 0x1.abc9e3b39803fp-56, r);
   // exp(r) by the degree-13 Taylor polynomial, coefficients RN(1/i!), Horner
-  double p = 0x1.6124613a86d09p-33;          // 1/13!
-  p = __builtin_fma(p, r, 0x1.1eed8eff8d898p-29);  // 1/12!
-  p = __builtin_fma(p, r, 0x1.ae64567f544e4p-26);  // 1/11!
-  p = __builtin_fma(p, r, 0x1.27e4fb7789f5cp-22);  // 1/10!
-  p = __builtin_fma(p, r, 0x1.71de3a556c734p-19);  // 1/9!
-  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-16);  // 1/8!
-  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-13);  // 1/7!
-  p = __builtin_fma(p, r, 0x1.6c16c16c16c17p-10);  // 1/6!
-  p = __builtin_fma(p, r, 0x1.1111111111111p-7);   // 1/5!
-  p = __builtin_fma(p, r, 0x1.5555555555555p-5);   // 1/4!
-  p = __builtin_fma(p, r, 0x1.5555555555555p-3);   // 1/3!
-  p = __builtin_fma(p, r, 0x1.0p-1);               // 1/2!
+  double p = kExpTaylor[0];
+#pragma unroll
+  for (int i = 1; i < 12; ++i) p = __builtin_fma(p, r, kExpTaylor[i]);
   p = __builtin_fma(p, r, 1.0);                    // 1/1!
   p = __builtin_fma(p, r, 1.0);                    // 1/0!
   // 2^n is exact: -58 <= n <= 151 here
