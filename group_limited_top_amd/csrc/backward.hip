@@ -753,10 +753,12 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
   for (int j = 0; j < kMaxK; ++j) slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;  // -1: skipped
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
-    const u32x4 vs = a.swg ? ld16(a.dxp + (size_t)(a.P + t) * H + h0) : zero4;
+    // every row is read once: nontemporal loads (as in the forward combine)
+    const u32x4 vs = a.swg ? ld16_stream(a.dxp + (size_t)(a.P + t) * H + h0) : zero4;
     u32x4 v[kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) v[j] = slot[j] >= 0 ? ld16(a.dxp + (size_t)slot[j] * H + h0) : zero4;
+    for (int j = 0; j < kMaxK; ++j)
+      v[j] = slot[j] >= 0 ? ld16_stream(a.dxp + (size_t)slot[j] * H + h0) : zero4;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
