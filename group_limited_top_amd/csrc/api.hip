@@ -295,8 +295,9 @@ int moe_layer_backward(const moe_desc_t* desc, const void* x, const moe_weights_
   int32_t* pair_slot = at<int32_t>(ws, L.pair_slot);
   int32_t* tile_off = at<int32_t>(ws, L.tile_off);
   int32_t* tile_tab = at<int32_t>(ws, L.tile_tab);
+  const int tile_rows = moe::bwd_tile_rows(d.T, d.top_k, d.E, d.I, d.I_shared, d.H);
   rc = hip_rc(moe::launch_permute(topk_idx, (int64_t)d.T * d.top_k, d.E, d.T, d.I_shared,
-                                  moe::kBwdTileRows, at<int32_t>(ws, L.perm),
+                                  tile_rows, at<int32_t>(ws, L.perm),
                                   at<int32_t>(ws, L.counts), offsets, sorted_pair, pair_slot,
                                   nullptr, tile_off, tile_tab, at<uint32_t>(ws, L.status),
                                   stream));
@@ -324,6 +325,7 @@ int moe_layer_backward(const moe_desc_t* desc, const void* x, const moe_weights_
   in.pair_slot = pair_slot;
   in.tile_off = tile_off;
   in.tile_tab = tile_tab;
+  in.tile_rows = tile_rows;
   in.scratch = at<void>(ws, L.inter);
   in.dx = static_cast<uint16_t*>(dx);
   in.dw_router = dw_router;

@@ -6,7 +6,11 @@
 namespace moe {
 
 // Backward --------------------------------------------------------------------
-constexpr int kBwdTileRows = 64;  // row tiles of the backward's grouped GEMMs
+constexpr int kBwdTileRows = 64;  // row tiles of the backward's own grouped GEMMs
+// Rows per tile the backward's permute builds: kGRows when the row products
+// run on the forward's expert GEMM (many rows per expert, bwd_gemm_ok),
+// kBwdTileRows for the backward's own row GEMMs otherwise.
+int bwd_tile_rows(int64_t T, int K, int E, int I, int Is, int H);
 struct BwdInputs {
   int T, H, E, K, I;  // I: routed = shared intermediate size (or no shared expert)
   float scale;
@@ -17,6 +21,7 @@ struct BwdInputs {
   const uint16_t *wg, *wu, *wd;    // [E][I][H]
   const uint16_t *swg, *swu, *swd; // [I][H] or null
   const int32_t *offsets, *sorted_pair, *pair_slot, *tile_off, *tile_tab;  // permute output
+  int tile_rows;                // the tiles' rows (bwd_tile_rows)
   void* scratch;                // bwd_intermediate_bytes
   uint16_t* dx;                 // [T][H]
   float* dw_router;             // [E][H]

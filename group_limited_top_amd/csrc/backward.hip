@@ -16,17 +16,20 @@
 //   dW_r[e] = sum over e's pairs of dlam * x.
 // Rows are the expert-sorted pairs (then the T shared rows), as in the forward.
 //
-// Steps: permute (the forward's kernels, 64-row tiles) -> k_bwd_gemm<kRowsNT>
-// (g = x W_g^T, u = x W_u^T, r = dy W_d^T, fp32) -> k_bwd_act (per row:
-// a, dL/dw, d_g, d_u, w a in bf16) -> k_bwd_router (per token: dlam) ->
-// k_bwd_gemm<kRowsNN> (per-row dx = d_g W_g + d_u W_u + dlam W_r[e], bf16) ->
+// Steps: permute (the forward's kernels) -> k_bwd_gemm<kRowsNT> (g = x W_g^T,
+// u = x W_u^T, r = dy W_d^T, fp32) -> k_bwd_act (per row: a, dL/dw, d_g, d_u,
+// w a in bf16) -> k_bwd_router (per token: dlam) -> k_bwd_gemm<kRowsNN>
+// (per-row dx = d_g W_g + d_u W_u, bf16) ->
 // k_bwd_wgrad<2, 64> (dW_gate, dW_up) and k_bwd_wgrad<1, *> (dW_down) per
 // expert, fp32, summed over the expert's rows in order ->
 // k_bwd_router_wgrad + k_bwd_router_reduce
 // (dW_r = dlogit^T x over token chunks, then the chunks in order) ->
 // k_bwd_combine (dx per token: shared row, then the K pair rows in j order,
-// fp32, one rounding).  Every sum has a fixed order: the results are
-// bit-reproducible.
+// then the router's share sum_j dlam_j W_r[e_j] in j order, fp32, one
+// rounding).  Every sum has a fixed order: the results are bit-reproducible.
+// With many rows per expert (bwd_tile_rows == kGRows) the two row products
+// run on the forward's persistent DMA-ring expert GEMM instead (k_expert_gemm
+// modes 2-4, 256-row tiles; launch_bwd_gur_gemm, launch_bwd_dx_gemm).
 //
 // Block order: the row-tile GEMMs give each XCD a contiguous run of (row
 // tile, column tile) items, expert by expert and column-major within one, so
@@ -316,20 +319,6 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_gemm(const BwdArgs a) {
 
   // acc[i][j][c] = C[A row 16 i + r16][B row wv * BN / 4 + 16 j + 4 q + c]
   const int q = lane >> 4, r16 = lane & 15;
-  // kRowsNN, routed rows: + dlam of the row's pair times W_r[e] (the router's
-  // share of dx), added before the one rounding to bf16
-  float rdl[4] = {};
-  f32x4 rw[TN] = {};
-  if (MODE == kRowsNN && !sh) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ar = 16 * i + r16;
-      rdl[i] = ar < nrows ? a.dlam[a.sorted_pair[orow + ar]] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      rw[j] = *reinterpret_cast<const f32x4*>(a.w_router + (size_t)e * H + n0 + wv * (BN / 4) + 16 * j + 4 * q);
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ar = 16 * i + r16;  // A row in the tile
@@ -342,8 +331,8 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_gemm(const BwdArgs a) {
         *reinterpret_cast<f32x4*>(out + (size_t)(orow + ar) * I + n0 + bc) = acc[i][j];
       } else {
         u32x2 pk;
-        pk.x = pack_bf16x2(acc[i][j][0] + rdl[i] * rw[j][0], acc[i][j][1] + rdl[i] * rw[j][1]);
-        pk.y = pack_bf16x2(acc[i][j][2] + rdl[i] * rw[j][2], acc[i][j][3] + rdl[i] * rw[j][3]);
+        pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
         *reinterpret_cast<u32x2*>(a.dxp + (size_t)(orow + ar) * H + n0 + bc) = pk;
       }
     }
@@ -741,16 +730,21 @@ __global__ __launch_bounds__(256) void k_bwd_router_reduce(const BwdArgs a, int 
   *reinterpret_cast<f32x4*>(a.dw_router + i) = acc;
 }
 
-// dx[t] = shared row + the pair rows in j order (each already holding its
-// router term); each thread 8 consecutive h, every row's load in flight
-// before the sums.
+// dx[t] = shared row + the pair rows in j order + the router's share
+// sum_j dlam_j W_r[e_j] in j order (fp32, one rounding); each thread 8
+// consecutive h, every pair row's load in flight before the sums.
 __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
   constexpr int kMaxK = 16;
   const int t = blockIdx.x;
   const int H = a.H, K = a.K;
-  int32_t slot[kMaxK];
+  int32_t slot[kMaxK], eix[kMaxK];
+  float dl[kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;  // -1: skipped
+  for (int j = 0; j < kMaxK; ++j) {
+    slot[j] = j < K ? a.pair_slot[(size_t)t * K + j] : -1;  // -1: skipped
+    eix[j] = j < K ? a.idx[(size_t)t * K + j] : 0;
+    dl[j] = j < K ? a.dlam[(size_t)t * K + j] : 0.0f;
+  }
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
     // every row is read once: nontemporal loads (as in the forward combine)
@@ -776,6 +770,28 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const BwdArgs a) {
         acc[2 * i + 1] += bf16_hi(v[j][i]);
       }
     }
+    // the router's share: dlam_j W_r[e_j] in j order, 4 pairs' W_r pieces in
+    // flight at a time (W_r, 4 bytes an element, stays in L2)
+#pragma unroll
+    for (int j0 = 0; j0 < kMaxK; j0 += 4) {
+      if (j0 >= K) break;  // block-uniform
+      f32x4 wr[4][2];
+#pragma unroll
+      for (int j = j0; j < j0 + 4; ++j) {
+        const float* row = a.w_router + (size_t)(slot[j] >= 0 ? eix[j] : 0) * H + h0;
+        wr[j - j0][0] = slot[j] >= 0 ? *reinterpret_cast<const f32x4*>(row) : f32x4{0.f, 0.f, 0.f, 0.f};
+        wr[j - j0][1] = slot[j] >= 0 ? *reinterpret_cast<const f32x4*>(row + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = j0; j < j0 + 4; ++j) {
+        if (slot[j] < 0) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[c] += dl[j] * wr[j - j0][0][c];
+          acc[4 + c] += dl[j] * wr[j - j0][1][c];
+        }
+      }
+    }
     u32x4 pk;
     pk.x = pack_bf16x2(acc[0], acc[1]);
     pk.y = pack_bf16x2(acc[2], acc[3]);
@@ -793,11 +809,23 @@ static int router_chunks(int64_t T) {
   return (int)std::min<int64_t>(kRwChunkMax, std::max<int64_t>(1, (T + kRwStep - 1) / kRwStep));
 }
 
+int bwd_tile_rows(int64_t T, int K, int E, int I, int Is, int H) {
+  return expert_tile_rows(T, K, E, I, Is, H, true) == kGRows && bwd_gemm_ok(T, K, I, Is, H)
+             ? kGRows
+             : kBwdTileRows;
+}
+
+// The trash area of the expert GEMM's backward modes (8 KiB per XCD slot).
+constexpr size_t kBwdTrashBytes = 65536;
+
 size_t bwd_intermediate_bytes(int64_t T, int K, int E, int I, int H, bool shared) {
   const size_t rows = (size_t)(T * K + (shared ? T : 0));
   auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-  return 3 * al(rows * I * 4) + 3 * al(rows * I * 2) + 2 * al((size_t)T * K * 4) +
-         al(rows * H * 2) + al((size_t)router_chunks(T) * E * H * 4);
+  // d_g and d_u carry kGRows rows of padding: the expert GEMM reads whole
+  // 256-row tiles of them
+  return 3 * al(rows * I * 4) + 2 * al((rows + kGRows) * I * 2) + al(rows * I * 2) +
+         2 * al((size_t)T * K * 4) + al(rows * H * 2) + al((size_t)router_chunks(T) * E * H * 4) +
+         al(kBwdTrashBytes);
 }
 
 hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
@@ -844,27 +872,66 @@ hipError_t launch_backward(const BwdInputs& in, hipStream_t s) {
   a.g = reinterpret_cast<float*>(take((size_t)rows * a.I * 4));
   a.u = reinterpret_cast<float*>(take((size_t)rows * a.I * 4));
   a.r = reinterpret_cast<float*>(take((size_t)rows * a.I * 4));
-  a.dg = reinterpret_cast<uint16_t*>(take((size_t)rows * a.I * 2));
-  a.du = reinterpret_cast<uint16_t*>(take((size_t)rows * a.I * 2));
+  a.dg = reinterpret_cast<uint16_t*>(take((size_t)(rows + kGRows) * a.I * 2));
+  a.du = reinterpret_cast<uint16_t*>(take((size_t)(rows + kGRows) * a.I * 2));
   a.aw = reinterpret_cast<uint16_t*>(take((size_t)rows * a.I * 2));
   a.gw = reinterpret_cast<float*>(take((size_t)a.P * 4));
   a.dlam = reinterpret_cast<float*>(take((size_t)a.P * 4));
   a.dxp = reinterpret_cast<uint16_t*>(take((size_t)rows * a.H * 2));
   const int nchunk = router_chunks(a.T);
   float* rpart = reinterpret_cast<float*>(take((size_t)nchunk * a.E * a.H * 4));
+  void* trash = take(kBwdTrashBytes);
   const int chunk = (int)(((a.T + nchunk - 1) / nchunk + kRwStep - 1) / kRwStep * kRwStep);
 
   // row tiles: a host upper bound; blocks past the count the permute wrote exit
-  const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, shared ? a.I : 0, kBwdTileRows);
+  const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, shared ? a.I : 0, in.tile_rows);
   a.rtiles = (int)rtiles;
   auto grid8 = [](int64_t n) { return dim3((unsigned)((n + 7) / 8 * 8)); };
-  if (a.I % 256 == 0)
+  // many rows per expert: the row products on the forward's expert GEMM
+  const bool gemm = in.tile_rows == kGRows;
+  ExpertArgs ea{};
+  if (gemm) {
+    ea.T = a.T;
+    ea.H = a.H;
+    ea.E = a.E;
+    ea.K = a.K;
+    ea.I = a.I;
+    ea.Is = shared ? a.I : 0;
+    ea.x = a.x;
+    ea.sorted_pair = a.sorted_pair;
+    ea.w_gate = a.wg;
+    ea.w_up = a.wu;
+    ea.w_down = a.wd;
+    ea.ws_gate = a.swg;
+    ea.ws_up = a.swu;
+    ea.ws_down = a.swd;
+    ea.tile_off = const_cast<int32_t*>(a.tile_off);
+    ea.tile_tab = const_cast<int32_t*>(a.tile_tab);
+    ea.tile_rows = kGRows;
+    ea.tiles_ready = true;
+    ea.dy = a.dy;
+    ea.bwd_g = a.g;
+    ea.bwd_u = a.u;
+    ea.bwd_r = a.r;
+    ea.bwd_dg = a.dg;
+    ea.bwd_du = a.du;
+    ea.bwd_dx = a.dxp;
+    ea.trash = trash;
+    const hipError_t e = launch_bwd_gur_gemm(ea, s);
+    if (e != hipSuccess) return e;
+  } else if (a.I % 256 == 0) {
     hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 256>), grid8(rtiles * (3 * a.I / 256)), dim3(kBT), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((k_bwd_gemm<kRowsNT, 64>), grid8(rtiles * (3 * a.I / 64)), dim3(kBT), 0, s, a);
+  }
   hipLaunchKernelGGL(k_bwd_act, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, (int)rows);
   hipLaunchKernelGGL(k_bwd_router, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((k_bwd_gemm<kRowsNN, 256>), grid8(rtiles * (a.H / 256)), dim3(kBT), 0, s, a);
+  if (gemm) {
+    const hipError_t e = launch_bwd_dx_gemm(ea, s);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((k_bwd_gemm<kRowsNN, 256>), grid8(rtiles * (a.H / 256)), dim3(kBT), 0, s, a);
+  }
   {
     auto grid_w = [&](int aw) {
       const int64_t per = (a.I / aw) * (a.H / 256);

@@ -18,6 +18,11 @@
 //            [I][H] (H contiguous), and the LDS transpose read
 //            (ds_read_b64_tr_b16) turns its staged [k][column] rows into the
 //            MFMA operand (4 consecutive k of one column per lane).  K = I.
+// The layer backward's row products run on the same kernel: g, u (the
+// gate/up products kept apart, fp32), r = dy W_down^T (a gate-shaped product:
+// dy rows against W_down's rows, 256 features a tile, fp32), and dx per row =
+// d_g W_gate + d_u W_up (a down-shaped product with K = 2 I: the d_g rows
+// against W_gate, then the d_u rows against W_up; bf16).
 //
 // Data path.  A step is 64 deep in K, so every staged row is one whole
 // 128-byte line (half lines halve what the load path delivers per CU).  The
@@ -94,10 +99,16 @@ __device__ __forceinline__ GTile gtile(const int32_t* tab, int t, int S) {
   return g;
 }
 
-// MODE 0: gate/up + SwiGLU; MODE 1: down.
+// MODE 0: gate/up + SwiGLU; MODE 1: down; the backward's MODE 2: g, u;
+// MODE 3: r; MODE 4: dx.
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int S) {
-  constexpr int kStores = 16;  // epilogue stores per wave (8 bytes each for gate/up, 16 for down)
+  // modes 0, 2, 3: K = H, gathered token rows against K-contiguous weight rows;
+  // modes 1, 4: contiguous h rows against N-contiguous weights
+  constexpr bool kGU = MODE == 0 || MODE == 2 || MODE == 3;
+  // epilogue stores per wave: 8 bytes each (mode 0), 16 (modes 1, 4), 16-byte
+  // fp32 pieces (modes 2, 3)
+  constexpr int kStores = (MODE == 2 || MODE == 3) ? 32 : 16;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingN * kSliceB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,9 +118,11 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // the operand arrays, read once from the kernel arguments into scalar
   // registers (selecting among struct fields later would otherwise become a
   // vector load of the argument block)
-  const uint8_t* const x_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.x));
-  const uint8_t* const hr_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.h_routed));
+  const uint8_t* const x_p = uniform_ptr(reinterpret_cast<const uint8_t*>(MODE == 3 ? a.dy : a.x));
+  const uint8_t* const hr_p =
+      uniform_ptr(reinterpret_cast<const uint8_t*>(MODE == 4 ? a.bwd_dg : a.h_routed));
   const uint8_t* const hs_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.h_shared));
+  const uint8_t* const hu_p = uniform_ptr(reinterpret_cast<const uint8_t*>(a.bwd_du));  // mode 4
   const uint16_t* const wg_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_gate));
   const uint16_t* const wu_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_up));
   const uint16_t* const wd_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.w_down));
@@ -118,8 +131,12 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   const uint16_t* const sd_p = uniform_ptr(reinterpret_cast<const uint16_t*>(a.ws_down));
   const int32_t* const sp_p = uniform_ptr(a.sorted_pair);
   uint16_t* const hrw_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.h_routed));
-  uint16_t* const orw_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.o_routed));
-  uint16_t* const osw_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.o_shared));
+  uint16_t* const orw_p = uniform_ptr(reinterpret_cast<uint16_t*>(MODE == 4 ? a.bwd_dx : a.o_routed));
+  uint16_t* const osw_p = MODE == 4 ? orw_p + (size_t)a.T * a.K * a.H
+                                    : uniform_ptr(reinterpret_cast<uint16_t*>(a.o_shared));
+  float* const bo_p = uniform_ptr(MODE == 2 ? a.bwd_g : a.bwd_r);  // modes 2, 3
+  float* const bu_p = uniform_ptr(a.bwd_u);                          // mode 2
+  uint16_t* const btr_p = uniform_ptr(reinterpret_cast<uint16_t*>(a.trash));
   const int T = a.T, K = a.K;
   const int32_t* const tab_p = uniform_ptr(a.tile_tab);
   const int32_t* const toff_p = uniform_ptr(a.tile_off);
@@ -129,10 +146,13 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // then pick with an integer select (a select between two captured pointers
   // would become a load through a select of their addresses, which keeps
   // them in private memory).
-  const uint16_t* const wgu_p = w < 4 ? wg_p : wu_p;            // this wave's gate or up
-  const ptrdiff_t sh_wgu = (w < 4 ? sg_p : su_p) - wgu_p;        // shared minus routed
+  // this wave's gate or up rows (mode 3: W_down's, both halves of the tile)
+  const uint16_t* const wgu_p = MODE == 3 ? wd_p : w < 4 ? wg_p : wu_p;
+  const ptrdiff_t sh_wgu = (MODE == 3 ? sd_p : w < 4 ? sg_p : su_p) - wgu_p;  // shared minus routed
   const ptrdiff_t sh_wd = sd_p - wd_p;
-  const ptrdiff_t sh_h = hs_p - hr_p;   // bytes
+  const ptrdiff_t sh_wg = sg_p - wg_p, sh_wu = su_p - wu_p;  // mode 4
+  // mode 4: the shared rows follow the P routed rows of d_g and d_u
+  const ptrdiff_t sh_h = MODE == 4 ? (ptrdiff_t)a.T * a.K * a.I * 2 : hs_p - hr_p;  // bytes
   const ptrdiff_t sh_hw = sh_h / 2;      // bf16 elements (both arrays are 256-byte aligned)
   const ptrdiff_t sh_o = osw_p - orw_p;
 
@@ -144,7 +164,8 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   const int first = lo + (int)(blockIdx.x >> 3);
   if (first >= hi) return;
   const int count = (hi - first + nbx - 1) / nbx;
-  const int nsteps = (MODE == 0 ? H : I) / kGK;
+  const int nI = I / kGK;  // mode 4: steps against W_gate, then as many against W_up
+  const int nsteps = kGU ? H / kGK : MODE == 4 ? 2 * nI : nI;
   const int total = count * nsteps;  // steps of this block
   const int nslices = 2 * total;     // slice 2s: token rows of step s, 2s + 1: weights
   const uint32_t ring0 = __builtin_amdgcn_readfirstlane(
@@ -160,10 +181,12 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // weights
   int wmi = -1, wk = 0;
   const uint8_t* wb = nullptr;
+  const uint8_t* wb2 = nullptr;  // mode 4: W_up
+  const uint8_t* xb2 = nullptr;  // mode 4: the d_u rows
   uint32_t wo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (MODE == 0) {
+    if (kGU) {
       // gate (w < 4) or up rows 32 (w & 3) + 8 j + lane / 8 of the tile's features
       wo[j] = (uint32_t)((8 * j + (lane >> 3)) * H * 2 + rs_chunk(j, lane) * 16);
     } else {
@@ -184,7 +207,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
     const GTile g = gtile(tab_p, t, S);
     pe = g.e;
     prow0 = g.row0;
-    if (MODE == 0 && g.e < E) {
+    if (kGU && g.e < E) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int32_t v = 0;
@@ -201,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   auto issue_x = [&](uint32_t lds) __attribute__((always_inline)) {
     if (xk == 0) {
       ++xm;
-      if (MODE == 0) {
+      if (kGU) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tok = pe < E ? ptok[j] / K : prow0 + 32 * w + 8 * j + (lane >> 3);
@@ -210,10 +233,12 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
         xb = x_p;
       } else {
         xb = uniform_ptr(hr_p + (pe < E ? 0 : sh_h) + (size_t)prow0 * I * 2);
+        if (MODE == 4) xb2 = uniform_ptr(hu_p + (pe < E ? 0 : sh_h) + (size_t)prow0 * I * 2);
       }
       if (xm + 1 < count) fetch_rows(first + (xm + 1) * nbx);
     }
-    dma4(xb + xk * 128, xo, lds);
+    if (MODE == 4 && xk >= nI) dma4(xb2 + (xk - nI) * 128, xo, lds);
+    else dma4(xb + xk * 128, xo, lds);
     if (++xk == nsteps) xk = 0;
   };
   auto issue_w = [&](uint32_t lds) __attribute__((always_inline)) {
@@ -222,17 +247,25 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
       const GTile g = gtile(tab_p, first + wmi * nbx, S);
       const bool sh = g.e >= E;
       const size_t ebase = sh ? 0 : (size_t)g.e * I * H;
-      if (MODE == 0) {
+      if (kGU) {
         const uint16_t* src = wgu_p + (sh ? sh_wgu : 0);
-        wb = uniform_ptr(reinterpret_cast<const uint8_t*>(
-            src + ebase + (size_t)(g.s * kGuFeat + 32 * (w & 3)) * H));
+        // mode 3: 256 W_down rows a tile, waves 4..7 the second 128
+        const int row = MODE == 3 ? g.s * 2 * kGuFeat + kGuFeat * (w >> 2) + 32 * (w & 3)
+                                  : g.s * kGuFeat + 32 * (w & 3);
+        wb = uniform_ptr(reinterpret_cast<const uint8_t*>(src + ebase + (size_t)row * H));
+      } else if (MODE == 4) {
+        wb = uniform_ptr(reinterpret_cast<const uint8_t*>(wg_p + (sh ? sh_wg : 0) + ebase +
+                                                          (size_t)g.s * kDnOut));
+        wb2 = uniform_ptr(reinterpret_cast<const uint8_t*>(wu_p + (sh ? sh_wu : 0) + ebase +
+                                                           (size_t)g.s * kDnOut));
       } else {
         const uint16_t* src = wd_p + (sh ? sh_wd : 0);
         wb = uniform_ptr(reinterpret_cast<const uint8_t*>(src + ebase + (size_t)g.s * kDnOut));
       }
     }
-    const size_t step_bytes = MODE == 0 ? 128 : (size_t)kGK * H * 2;
-    dma4(wb + wk * step_bytes, wo, lds);
+    const size_t step_bytes = kGU ? 128 : (size_t)kGK * H * 2;
+    if (MODE == 4 && wk >= nI) dma4(wb2 + (wk - nI) * step_bytes, wo, lds);
+    else dma4(wb + wk * step_bytes, wo, lds);
     if (++wk == nsteps) wk = 0;
   };
   // Slice sigma goes to buffer sigma % 5; slice 2 s holds the token rows of
@@ -263,7 +296,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     lane_b[h] = rs_addr(64 * wm + r16, 4 * h + q);
-    if (MODE == 0) {
+    if (kGU) {
       lane_a[h] = rs_addr(64 * wn + r16, 4 * h + q);
     } else {
       const int r = 32 * h + 8 * q + (r16 >> 2);
@@ -277,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // MFMAs.  The second half's reads are thus hidden behind MFMAs; 64 operand
   // registers where two full sets would need 96.
   auto read_a = [&](const uint8_t* bw, int i) __attribute__((always_inline)) {
-    if (MODE == 0) {
+    if (kGU) {
       return lds16(bw + (i < 4 ? 2048 * i : 16384 + 2048 * (i - 4)));
     } else {
       const uint8_t* p = bw + 8 * (i & 1) + ((dn_v ^ (4 * (i >> 1))) << 4);
@@ -310,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, MODE == 0 ? 1 : 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kGU ? 1 : 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
   };
@@ -319,7 +352,8 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
   // contents are never used), so that the ring's waits can count them.
   // Each lane has its own 16 bytes of trash (blocks spread over the padding
   // rows), so the dropped stores do not all hit one line.
-  uint16_t* const trash = hrw_p + (size_t)T * K * I + (size_t)(blockIdx.x & 7) * 4096 + 8 * tid;
+  uint16_t* const trash = (MODE >= 2 ? btr_p : hrw_p + (size_t)T * K * I) +
+                         (size_t)(blockIdx.x & 7) * 4096 + 8 * tid;
   auto epilogue = [&](int m) __attribute__((always_inline)) {
     const GTile g = gtile(tab_p, first + m * nbx, S);
     const bool sh = g.e >= E;
@@ -341,6 +375,28 @@ __global__ __launch_bounds__(512, 1) void k_expert_gemm(const ExpertArgs a, int 
           pk.y = pack_bf16x2(hv[2], hv[3]);
           uint16_t* dst = ok ? hb + (size_t)16 * n * Iw + 16 * i : trash;
           store8(dst, pk);
+        }
+      }
+    } else if (MODE == 2 || MODE == 3) {
+      // fp32 rows: a routed tile's at its sorted rows, a shared one's after
+      // the P routed rows.  The lane holds 4 consecutive features of each
+      // column tile i: mode 2 g (i < 4) and u (i >= 4) of features 64 wn +
+      // 16 (i % 4) + 4 q of the slice; mode 3 r of features 64 wn + 16 i +
+      // 4 q (i < 4) and 128 + 64 wn + 16 (i - 4) + 4 q.
+      const size_t orow = (sh ? (size_t)T * K : 0) + (size_t)(g.row0 + rr);
+      const int f0 = g.s * (MODE == 2 ? kGuFeat : 2 * kGuFeat) + 64 * wn + 4 * q;
+      float* const ob = bo_p + orow * I + f0;
+      float* const ub = bu_p + orow * I + f0;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bool ok = rr + 16 * n < g.nrows;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float* dst;
+          if (MODE == 2) dst = (i < 4 ? ob : ub) + (size_t)16 * n * I + 16 * (i & 3);
+          else dst = ob + (size_t)16 * n * I + (i < 4 ? 16 * i : kGuFeat + 16 * (i - 4));
+          *(__attribute__((address_space(1))) f32x4*)(ok ? dst : reinterpret_cast<float*>(trash)) =
+              acc[i][n];
         }
       }
     } else {
@@ -427,6 +483,14 @@ static int cu_count() {
   return n;
 }
 
+// One persistent block per CU (a multiple of 8, so that every XCD has as
+// many), fewer when there are fewer tiles.
+static dim3 gemm_grid(int64_t tiles) {
+  const int cus = cu_count() / 8 * 8;
+  const int64_t g = tiles < cus ? (tiles + 7) / 8 * 8 : cus;
+  return dim3((unsigned)(g > 0 ? g : 8));
+}
+
 hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm) {
   if (a.tile_rows != kGRows || !gemm_shape_ok(a.T, a.K, a.I, a.Is, a.H)) return hipErrorInvalidValue;
   if (!a.tiles_ready) {
@@ -437,11 +501,7 @@ hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const St
   }
   const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
   const int gu_slices = a.I / kGuFeat, dn_slices = a.H / kDnOut;
-  const int cus = cu_count() / 8 * 8;
-  auto grid = [&](int64_t tiles) __attribute__((always_inline)) {
-    int64_t g = tiles < cus ? (tiles + 7) / 8 * 8 : cus;
-    return dim3((unsigned)(g > 0 ? g : 8));
-  };
+  auto grid = gemm_grid;
   stage_begin(tm, kGateUp, s);
   hipLaunchKernelGGL(k_expert_gemm<0>, grid(rtiles * gu_slices), dim3(512), 0, s, a, gu_slices);
   stage_end(tm, kGateUp, s);
@@ -451,6 +511,30 @@ hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const St
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine_bf16(a, s, tm);
+}
+
+bool bwd_gemm_ok(int64_t T, int K, int I, int Is, int H) {
+  // r's tiles are 256 features wide
+  return gemm_shape_ok(T, K, I, Is, H) && I % (2 * kGuFeat) == 0;
+}
+
+hipError_t launch_bwd_gur_gemm(const ExpertArgs& a, hipStream_t s) {
+  if (a.tile_rows != kGRows || !bwd_gemm_ok(a.T, a.K, a.I, a.Is, a.H) || !a.trash)
+    return hipErrorInvalidValue;
+  const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
+  const int gu = a.I / kGuFeat, rs = a.I / (2 * kGuFeat);
+  hipLaunchKernelGGL(k_expert_gemm<2>, gemm_grid(rtiles * gu), dim3(512), 0, s, a, gu);
+  hipLaunchKernelGGL(k_expert_gemm<3>, gemm_grid(rtiles * rs), dim3(512), 0, s, a, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx_gemm(const ExpertArgs& a, hipStream_t s) {
+  if (a.tile_rows != kGRows || !bwd_gemm_ok(a.T, a.K, a.I, a.Is, a.H) || !a.trash)
+    return hipErrorInvalidValue;
+  const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
+  const int dn = a.H / kDnOut;
+  hipLaunchKernelGGL(k_expert_gemm<4>, gemm_grid(rtiles * dn), dim3(512), 0, s, a, dn);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -73,11 +73,25 @@ struct ExpertArgs {
   void* h_shared;     // [T][Is]
   void* o_routed;     // [P][H]
   void* o_shared;     // [T][H]
+  // the backward's row products (k_expert_gemm modes 2-4); their rows are
+  // the sorted pairs, then the T shared rows
+  const void* dy;          // [T][H] upstream gradient (mode 3's token rows)
+  float *bwd_g, *bwd_u;    // [P + T][I] fp32 (mode 2)
+  float* bwd_r;            // [P + T][I] fp32 (mode 3)
+  const void *bwd_dg, *bwd_du;  // [P + T + kGRows][I] bf16 (mode 4's rows)
+  void* bwd_dx;            // [P + T][H] bf16 (mode 4)
+  void* trash;             // >= 64 KiB: modes 2-4 send stores of rows past a tile's end here
 };
 int64_t max_expert_tiles(int64_t T, int64_t K, int E, int Is, int tile_rows);
 // LDS-pipelined MFMA GEMMs (tile_rows == kGRows); shapes with gemm_shape_ok.
 bool gemm_shape_ok(int64_t T, int K, int I, int Is, int H);
 hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const StageTimer* tm);
+// The backward's row products on the same GEMM (256-row tiles already built):
+// g, u = x W_g^T, x W_u^T and r = dy W_d^T (fp32), then dx per row =
+// d_g W_g + d_u W_u (bf16).  Usable when bwd_gemm_ok.
+bool bwd_gemm_ok(int64_t T, int K, int I, int Is, int H);
+hipError_t launch_bwd_gur_gemm(const ExpertArgs& a, hipStream_t s);
+hipError_t launch_bwd_dx_gemm(const ExpertArgs& a, hipStream_t s);
 // gate/up weight streaming through the LDS ring (32-row tiles); usable when
 // stream_ring_ok.
 bool stream_ring_ok(const ExpertArgs& a);

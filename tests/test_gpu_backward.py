@@ -153,6 +153,72 @@ def test_backward_full_size_sampled():
     assert r <= TOL
 
 
+def _takes_expert_gemm(shape):
+    """The backward runs its row products on the forward's expert GEMM
+    (256-row tiles) when a routed expert averages at least 128 rows, the
+    shared expert is as wide as the routed ones, and I is a multiple of 256
+    and H of 256."""
+    return (shape.T * shape.top_k // shape.E >= 128 and shape.I_shared == shape.I
+            and shape.I % 256 == 0 and shape.H % 256 == 0)
+
+
+# the expert-GEMM path: 256 experts at 128 rows each (the threshold), 64
+# experts with I = 512 (two r slices, ragged tiles), and a skew in which one
+# expert owns every token (many row tiles of one expert)
+@pytest.mark.parametrize("T,H,I,kw,skew", [
+    (4096, 512, 256, {}, False),
+    (2304, 512, 512, dict(E=64, n_group=4, topk_group=2, top_k=6), False),
+    (3000, 768, 256, dict(E=64, n_group=4, topk_group=2), True),
+])
+def test_backward_expert_gemm_path(T, H, I, kw, skew):
+    shape = synth.small_shape(T, H=H, I=I, I_shared=I, bias="normal", seed=700 + T, **kw)
+    assert _takes_expert_gemm(shape)
+    say("backward expert-GEMM path", T, H, I, kw, "skew" if skew else "")
+    dev = make_layer(shape)
+    if skew:
+        rng = np.random.default_rng(5)
+        idx = np.empty((T, shape.top_k), np.int32)
+        idx[:, 0] = 0
+        for t in range(T):
+            idx[t, 1:] = 1 + rng.choice(40, shape.top_k - 1, replace=False)
+        l64 = oracle.logits_any(nb(dev["x"]), nb(dev["w_router"]))
+    else:
+        idx, l64 = _routing(shape, dev)
+    dy = _dy(shape, 23 + T)
+    gpu = _gpu_backward(shape, dev, idx, l64, dy)
+    rng = np.random.default_rng(T)
+    tok = np.sort(rng.choice(T, 64, replace=False)).astype(np.int32)
+    tok[-1] = T - 1  # the last token: the shared expert's last, partial tile
+    tok = np.unique(tok)
+    ref = _check_tokens(shape, dev, idx, l64, dy, gpu, tok)
+    counts = np.bincount(idx.ravel(), minlength=shape.E)
+    for e in (int(np.argmax(counts)), int(np.argsort(counts)[len(counts) // 2]), shape.E):
+        _check_expert(shape, dev, idx, l64, dy, gpu, e)
+    # a router weight gradient row from the tokens that chose that expert
+    e = int(np.argmin(np.abs(counts - 40))) if not skew else 3
+    toks = np.nonzero((idx == e).any(axis=1))[0].astype(np.int32)
+    ref = oracle.backward_tokens(nb(dev["x"]), nb(dev["w_router"]), l64, idx, shape.scale,
+                                 dy.double().numpy(), *oracle_weights(dev), tokens=toks)
+    want = oracle.router_weight_grad(nb(dev["x"])[toks], ref["dlogit"])[e]
+    r = rel_l2(gpu["dw_router"][e].double().cpu().numpy(), want)
+    say("dw_router row", e, "rel_l2", r)
+    assert r <= TOL
+
+
+def test_backward_expert_gemm_path_deterministic():
+    shape = synth.small_shape(4096, H=512, I=256, I_shared=256, bias="normal", seed=931)
+    assert _takes_expert_gemm(shape)
+    say("backward expert-GEMM path determinism")
+    dev = make_layer(shape)
+    idx, l64 = _routing(shape, dev)
+    dy = _dy(shape, 4)
+    a = _gpu_backward(shape, dev, idx, l64, dy)
+    b = _gpu_backward(shape, dev, idx, l64, dy)
+    for k, v in a.items():
+        if v is not None:
+            assert torch.equal(v, b[k]), k
+
+
 def test_backward_skewed_routing():
     """Every token picks expert 0 and seven of experts 1..32: expert 0's rows
     are all the tokens (many row tiles of one expert, long weight-gradient
