@@ -501,12 +501,11 @@ hipError_t launch_experts_gemm_bf16(const ExpertArgs& a, hipStream_t s, const St
   }
   const int64_t rtiles = max_expert_tiles(a.T, a.K, a.E, a.Is, a.tile_rows);
   const int gu_slices = a.I / kGuFeat, dn_slices = a.H / kDnOut;
-  auto grid = gemm_grid;
   stage_begin(tm, kGateUp, s);
-  hipLaunchKernelGGL(k_expert_gemm<0>, grid(rtiles * gu_slices), dim3(512), 0, s, a, gu_slices);
+  hipLaunchKernelGGL(k_expert_gemm<0>, gemm_grid(rtiles * gu_slices), dim3(512), 0, s, a, gu_slices);
   stage_end(tm, kGateUp, s);
   stage_begin(tm, kDown, s);
-  hipLaunchKernelGGL(k_expert_gemm<1>, grid(rtiles * dn_slices), dim3(512), 0, s, a, dn_slices);
+  hipLaunchKernelGGL(k_expert_gemm<1>, gemm_grid(rtiles * dn_slices), dim3(512), 0, s, a, dn_slices);
   stage_end(tm, kDown, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

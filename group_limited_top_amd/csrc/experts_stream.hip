@@ -421,7 +421,8 @@ __device__ __forceinline__ void stream_body(const ExpertArgs& a, int S) {
               acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[t][j], B[n][j], acc[t][n], 0, 0, 0);
       }
     }
-  };  auto compute = [&](int c) __attribute__((always_inline)) {
+  };
+  auto compute = [&](int c) __attribute__((always_inline)) {
     if (((ring_rows >> (8 * (c & 3))) & 0xffu) > 16u)
       compute_nt(c, std::integral_constant<int, 2>());
     else
