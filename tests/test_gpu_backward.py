@@ -163,12 +163,14 @@ def _takes_expert_gemm(shape):
 
 
 # the expert-GEMM path: 256 experts at 128 rows each (the threshold), 64
-# experts with I = 512 (two r slices, ragged tiles), and a skew in which one
-# expert owns every token (many row tiles of one expert)
+# experts with I = 512 (two r slices, ragged tiles), a skew in which one
+# expert owns every token (many row tiles of one expert), and 512 experts
+# with top_k = 16 (the combine's router term over 16 pairs)
 @pytest.mark.parametrize("T,H,I,kw,skew", [
     (4096, 512, 256, {}, False),
     (2304, 512, 512, dict(E=64, n_group=4, topk_group=2, top_k=6), False),
     (3000, 768, 256, dict(E=64, n_group=4, topk_group=2), True),
+    (4100, 512, 256, dict(E=512, n_group=8, topk_group=4, top_k=16), False),
 ])
 def test_backward_expert_gemm_path(T, H, I, kw, skew):
     shape = synth.small_shape(T, H=H, I=I, I_shared=I, bias="normal", seed=700 + T, **kw)
